@@ -1,0 +1,171 @@
+/*
+ * swattn.h — C ABI of the sliding-window verify-attention library (MI355X / gfx950).
+ *
+ * The operation.  One call scores the n_q newest positions of B independent
+ * attention problems ("sequences"; a model's layers stacked along B count as
+ * separate problems) against a paged KV cache:
+ *
+ *   for b < B, i < n_q, h < H:
+ *     p   = ctx_len[b] - n_q            (position of the first new token)
+ *     t   = p + i                       (position of query i)
+ *     g   = h / (H / Hkv)               (grouped-query head mapping)
+ *     out[b][i][h] = sum_{t-window < j <= t} softmax_j(scale * q[b][i][h] . k_j) v_j
+ *     where k_j, v_j are row (j % block_size) of KV head g in physical block
+ *     block_table[b][j / block_size].
+ *
+ * Source: "The Fast Gemma Challenge: our verified-SOTA recipe, in full" (dev.to,
+ * VIDRAFT), full manifest.json — SLIDING_WINDOW=188 and FA_SLIDING=1 (attention
+ * over the most recent W tokens), SPECULATIVE_CONFIG with 7 MTP draft tokens (a
+ * verify step scores the target plus 7 drafts, each causal on the ones before
+ * it), SPLITKV_VERIFY / SPLITKV_VERIFY_MAX_Q=64 (the split-KV verify kernel takes
+ * at most 64 queries) and MAX_MODEL_LEN=4096; and its section "What each piece
+ * does, and why" (the window exists because decode is bound by KV-cache
+ * bandwidth; ONEGRAPH removes launch overhead, so calls must be capturable into
+ * a HIP graph).  Plain decode is n_q = 1.  The pages do not state whether the
+ * current token is inside the window; it is read here as included, so window = 1
+ * returns the query's own V row and window >= ctx_len is full causal attention.
+ *
+ * Threading and streams.  Every function is reentrant; the library keeps no
+ * state between calls.  swattn_verify enqueues at most two kernels on the given
+ * HIP stream and returns without synchronising or allocating, so it may be
+ * captured into a HIP graph.
+ */
+#ifndef SWATTN_H
+#define SWATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SWATTN_ABI_VERSION 1
+#define SWATTN_MAX_NQ 64          /* SPLITKV_VERIFY_MAX_Q of the manifest */
+
+typedef enum {
+    SWATTN_F32 = 0,               /* IEEE binary32 */
+    SWATTN_BF16 = 1,              /* bfloat16 (upper half of binary32) */
+    SWATTN_FP8_E4M3 = 2           /* OCP FP8 E4M3 ("e4m3fn"): bias 7, max 448, no inf */
+} swattn_dtype_t;
+
+typedef enum {
+    SWATTN_OK = 0,
+    SWATTN_ERR_NULL = -1,         /* a required pointer is NULL */
+    SWATTN_ERR_SHAPE = -2,        /* batch/heads/head_dim/block sizes invalid */
+    SWATTN_ERR_NQ = -3,           /* n_q outside [1, SWATTN_MAX_NQ] */
+    SWATTN_ERR_WINDOW = -4,       /* window < 1 */
+    SWATTN_ERR_DTYPE = -5,        /* unsupported dtype combination, or e4m3 without scales */
+    SWATTN_ERR_ALIGN = -6,        /* a data pointer is not 16-byte aligned */
+    SWATTN_ERR_WORKSPACE = -7,    /* workspace NULL or smaller than the plan needs */
+    SWATTN_ERR_CTX = -8,          /* a ctx_len outside [n_q, min(max_ctx_len, max_blocks*block_size)] */
+    SWATTN_ERR_BLOCK = -9,        /* a referenced block id outside [0, num_blocks) */
+    SWATTN_ERR_HIP = -10,         /* a HIP runtime call failed */
+    SWATTN_ERR_ARG = -11          /* other invalid argument (scale not finite, bad override) */
+} swattn_status_t;
+
+typedef enum {
+    SWATTN_VARIANT_AUTO = 0,
+    SWATTN_VARIANT_VALU = 1,      /* fp32 vector-ALU partition kernel (any dtype) */
+    SWATTN_VARIANT_MFMA = 2       /* bf16 matrix-core partition kernel (bf16 q, bf16/e4m3 kv) */
+} swattn_variant_t;
+
+/* Problem description.  Plain data; the caller owns it. */
+typedef struct {
+    int32_t batch;                /* B >= 1 independent problems */
+    int32_t num_heads;            /* H >= 1, a multiple of num_kv_heads */
+    int32_t num_kv_heads;         /* Hkv >= 1 */
+    int32_t head_dim;             /* D in {64, 128, 256} */
+    int32_t block_size;           /* KV positions per cache block, >= 1 */
+    int32_t max_blocks_per_seq;   /* row length of block_table, >= 1 */
+    int32_t num_blocks;           /* physical blocks in the KV pool, >= 1 */
+    int32_t max_ctx_len;          /* host-side upper bound of ctx_len[]; used to plan splits */
+    swattn_dtype_t q_dtype;       /* F32 or BF16 */
+    swattn_dtype_t kv_dtype;      /* F32, BF16 or FP8_E4M3 */
+    swattn_dtype_t out_dtype;     /* F32 or BF16 */
+    const float* k_scale;         /* [Hkv] device fp32, required iff kv_dtype == FP8_E4M3, else NULL */
+    const float* v_scale;         /* [Hkv] device fp32, same rule; stored value * scale = real value */
+    int32_t num_splits;           /* 0: library chooses; > 0 forces the KV split count */
+    int32_t variant;              /* swattn_variant_t; AUTO lets the library choose */
+} swattn_desc_t;
+
+/* What swattn_verify will launch for a description (filled by swattn_plan). */
+typedef struct {
+    int32_t variant;              /* SWATTN_VARIANT_VALU or SWATTN_VARIANT_MFMA */
+    int32_t num_splits;           /* S: KV splits per (problem, KV head, row chunk) */
+    int32_t rows_per_chunk;       /* query rows (n_q * H/Hkv packed) per workgroup */
+    int32_t row_chunks;           /* row chunks per (problem, KV head) */
+    int32_t grid;                 /* workgroups of the partition kernel */
+    int32_t merge_grid;           /* workgroups of the merge kernel (0 when S == 1) */
+    size_t workspace_bytes;       /* device scratch swattn_verify needs (0 when S == 1) */
+} swattn_plan_t;
+
+/*
+ * swattn_plan — validate a description and choose the launch.  Pure host code:
+ * no HIP call, no allocation; safe on a machine without a GPU.
+ * Returns SWATTN_OK and fills *plan, or an error code and leaves *plan untouched.
+ */
+swattn_status_t swattn_plan(const swattn_desc_t* desc, int32_t n_q, int32_t window,
+                            swattn_plan_t* plan);
+
+/* Convenience: workspace size in bytes for (desc, n_q, window); pure host code. */
+swattn_status_t swattn_workspace_bytes(const swattn_desc_t* desc, int32_t n_q, int32_t window,
+                                       size_t* bytes);
+
+/*
+ * swattn_verify — sliding-window attention for one verify (or decode) step.
+ *
+ *   q           [B][n_q][H][D]            q_dtype, device, read-only
+ *   k_cache     [num_blocks][Hkv][block_size][D]  kv_dtype, device, read-only
+ *   v_cache     same layout and dtype as k_cache
+ *   block_table [B][max_blocks_per_seq]   int32, device; entries past a sequence's
+ *                                         last block are never read
+ *   ctx_len     [B] int32, device; valid positions of sequence b, counting its
+ *               n_q new tokens, whose K/V must already be in the cache
+ *   n_q         1 .. SWATTN_MAX_NQ (1 = decode, 1 + drafts = verify)
+ *   window      >= 1 positions per query, the query's own position included
+ *   scale       finite softmax scale (usually 1/sqrt(D))
+ *   out         [B][n_q][H][D] out_dtype, device; fully overwritten; must not alias q
+ *   workspace   device scratch of >= plan.workspace_bytes (may be NULL when that is 0);
+ *               contents are undefined afterwards
+ *   stream      hipStream_t (NULL = default stream)
+ *
+ * All data pointers must be 16-byte aligned.  Host-checkable errors are returned
+ * before anything is enqueued.  Device-resident preconditions are not checked on
+ * this path (swattn_check_inputs does that): a sequence whose ctx_len lies
+ * outside [n_q, min(max_ctx_len, max_blocks_per_seq*block_size)] gets NaN in all
+ * its outputs, and a
+ * window position whose block id lies outside [0, num_blocks) is read as NaN, so
+ * bad inputs show in the output instead of faulting.  Launch failures return
+ * SWATTN_ERR_HIP; asynchronous faults surface on the stream.
+ */
+swattn_status_t swattn_verify(const swattn_desc_t* desc,
+                              const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_table, const int32_t* ctx_len,
+                              int32_t n_q, int32_t window, float scale,
+                              void* out, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/*
+ * swattn_check_inputs — debug check of the device-resident preconditions.
+ * Copies ctx_len and block_table to the host (synchronising the stream) and
+ * returns SWATTN_ERR_CTX if some ctx_len[b] lies outside
+ * [n_q, min(max_ctx_len, max_blocks_per_seq*block_size)], SWATTN_ERR_BLOCK if a block id that a
+ * window reads lies outside [0, num_blocks), SWATTN_OK otherwise.  Allocates
+ * host memory only; not for use under graph capture.
+ */
+swattn_status_t swattn_check_inputs(const swattn_desc_t* desc, const int32_t* block_table,
+                                    const int32_t* ctx_len, int32_t n_q, int32_t window,
+                                    void* stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* swattn_status_str(swattn_status_t status);
+
+/* SWATTN_ABI_VERSION of the loaded library. */
+int32_t swattn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SWATTN_H */

@@ -1,0 +1,143 @@
+// swattn_verify / swattn_check_inputs: host side of the C ABI.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <vector>
+
+#include "swattn.h"
+#include "swattn_internal.h"
+
+namespace swattn {
+swattn_status_t validate_desc(const swattn_desc_t* d, int32_t n_q, int32_t window);
+swattn_status_t make_plan(const swattn_desc_t* d, int32_t n_q, int32_t window, swattn_plan_t* out);
+
+namespace {
+
+bool aligned(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) == 0; }
+
+int dtype_bytes(int dt) { return dt == SWATTN_F32 ? 4 : (dt == SWATTN_BF16 ? 2 : 1); }
+
+}  // namespace
+}  // namespace swattn
+
+extern "C" swattn_status_t swattn_verify(const swattn_desc_t* d, const void* q, const void* k_cache,
+                                         const void* v_cache, const int32_t* block_table,
+                                         const int32_t* ctx_len, int32_t n_q, int32_t window, float scale,
+                                         void* out, void* workspace, size_t workspace_bytes, void* stream) {
+    using namespace swattn;
+    swattn_plan_t plan;
+    swattn_status_t st = make_plan(d, n_q, window, &plan);
+    if (st != SWATTN_OK) return st;
+    if (!q || !k_cache || !v_cache || !block_table || !ctx_len || !out) return SWATTN_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+        !aligned(block_table, 4) || !aligned(ctx_len, 4))
+        return SWATTN_ERR_ALIGN;
+    if (d->k_scale && (!aligned(d->k_scale, 4) || !aligned(d->v_scale, 4))) return SWATTN_ERR_ALIGN;
+    if (!std::isfinite(scale)) return SWATTN_ERR_ARG;
+
+    const int64_t G = d->num_heads / d->num_kv_heads;
+    const int64_t R = (int64_t)n_q * G;
+    const int64_t n_elems = (int64_t)d->batch * n_q * d->num_heads * d->head_dim;
+    // q and out must not overlap.
+    {
+        const uintptr_t q0 = reinterpret_cast<uintptr_t>(q);
+        const uintptr_t q1 = q0 + (uintptr_t)(n_elems * dtype_bytes(d->q_dtype));
+        const uintptr_t o0 = reinterpret_cast<uintptr_t>(out);
+        const uintptr_t o1 = o0 + (uintptr_t)(n_elems * dtype_bytes(d->out_dtype));
+        if (q0 < o1 && o0 < q1) return SWATTN_ERR_ARG;
+    }
+    float* ws_o = nullptr;
+    float* ws_lse = nullptr;
+    if (plan.workspace_bytes > 0) {
+        if (!workspace || workspace_bytes < plan.workspace_bytes) return SWATTN_ERR_WORKSPACE;
+        if (!aligned(workspace, 16)) return SWATTN_ERR_ALIGN;
+        const int64_t rows_total = (int64_t)d->batch * d->num_kv_heads * R;
+        const int64_t o_bytes = ((rows_total * plan.num_splits * d->head_dim * 4) + 255) / 256 * 256;
+        ws_o = reinterpret_cast<float*>(workspace);
+        ws_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + o_bytes);
+    }
+
+    PartitionParams p;
+    p.q = q;
+    p.k = k_cache;
+    p.v = v_cache;
+    p.block_table = block_table;
+    p.ctx_len = ctx_len;
+    p.k_scale = d->k_scale;
+    p.v_scale = d->v_scale;
+    p.out = out;
+    p.ws_o = ws_o;
+    p.ws_lse = ws_lse;
+    p.B = d->batch;
+    p.H = d->num_heads;
+    p.Hkv = d->num_kv_heads;
+    p.G = (int32_t)G;
+    p.D = d->head_dim;
+    p.bs = d->block_size;
+    p.max_blocks = d->max_blocks_per_seq;
+    p.num_blocks = d->num_blocks;
+    p.n_q = n_q;
+    p.window = window;
+    p.R = (int32_t)R;
+    p.max_ctx = d->max_ctx_len;
+    p.S = plan.num_splits;
+    p.rows_per_chunk = plan.rows_per_chunk;
+    p.row_chunks = plan.row_chunks;
+    p.q_dtype = d->q_dtype;
+    p.kv_dtype = d->kv_dtype;
+    p.out_dtype = d->out_dtype;
+    p.scale_log2 = (float)((double)scale * 1.4426950408889634);   // log2(e)
+
+    int err = plan.variant == SWATTN_VARIANT_MFMA ? launch_partition_mfma(p, plan.grid, stream)
+                                                  : launch_partition_valu(p, plan.grid, stream);
+    if (err != 0) return SWATTN_ERR_HIP;
+    if (plan.num_splits > 1) {
+        MergeParams m;
+        m.ws_o = ws_o;
+        m.ws_lse = ws_lse;
+        m.out = out;
+        m.B = d->batch;
+        m.H = d->num_heads;
+        m.Hkv = d->num_kv_heads;
+        m.G = (int32_t)G;
+        m.D = d->head_dim;
+        m.n_q = n_q;
+        m.R = (int32_t)R;
+        m.S = plan.num_splits;
+        m.out_dtype = d->out_dtype;
+        err = launch_merge(m, plan.merge_grid, stream);
+        if (err != 0) return SWATTN_ERR_HIP;
+    }
+    return SWATTN_OK;
+}
+
+extern "C" swattn_status_t swattn_check_inputs(const swattn_desc_t* d, const int32_t* block_table,
+                                               const int32_t* ctx_len, int32_t n_q, int32_t window,
+                                               void* stream) {
+    using namespace swattn;
+    swattn_status_t st = validate_desc(d, n_q, window);
+    if (st != SWATTN_OK) return st;
+    if (!block_table || !ctx_len) return SWATTN_ERR_NULL;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    std::vector<int32_t> ctx(d->batch);
+    std::vector<int32_t> table((size_t)d->batch * d->max_blocks_per_seq);
+    if (hipMemcpyAsync(ctx.data(), ctx_len, ctx.size() * 4, hipMemcpyDeviceToHost, s) != hipSuccess)
+        return SWATTN_ERR_HIP;
+    if (hipMemcpyAsync(table.data(), block_table, table.size() * 4, hipMemcpyDeviceToHost, s) != hipSuccess)
+        return SWATTN_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return SWATTN_ERR_HIP;
+    const int64_t cap = (int64_t)d->max_blocks_per_seq * d->block_size;
+    for (int b = 0; b < d->batch; ++b)
+        if (ctx[b] < n_q || ctx[b] > cap || ctx[b] > d->max_ctx_len) return SWATTN_ERR_CTX;
+    for (int b = 0; b < d->batch; ++b) {
+        const int64_t lo = std::max<int64_t>(0, (int64_t)ctx[b] - n_q - window + 1);
+        const int64_t hi = ctx[b] - 1;
+        for (int64_t blk = lo / d->block_size; blk <= hi / d->block_size; ++blk) {
+            const int32_t phys = table[(size_t)b * d->max_blocks_per_seq + blk];
+            if (phys < 0 || phys >= d->num_blocks) return SWATTN_ERR_BLOCK;
+        }
+    }
+    return SWATTN_OK;
+}

@@ -1,0 +1,158 @@
+// swattn_plan / swattn_workspace_bytes: argument validation and launch planning.
+// Pure host code: no HIP runtime call, no allocation.
+
+#include <algorithm>
+#include <climits>
+#include <cmath>
+#include <cstdint>
+#include <initializer_list>
+
+#include "swattn.h"
+#include "swattn_internal.h"
+
+namespace swattn {
+
+namespace {
+
+constexpr int64_t kFillTarget = 512;   // partition workgroups wanted in flight (2 per CU)
+
+bool dtype_in(int v, std::initializer_list<int> ok) {
+    for (int o : ok)
+        if (v == o) return true;
+    return false;
+}
+
+int64_t clamp64(int64_t v, int64_t lo, int64_t hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+}  // namespace
+
+swattn_status_t validate_desc(const swattn_desc_t* d, int32_t n_q, int32_t window) {
+    if (!d) return SWATTN_ERR_NULL;
+    if (d->batch < 1 || d->num_heads < 1 || d->num_kv_heads < 1 ||
+        d->num_heads % d->num_kv_heads != 0)
+        return SWATTN_ERR_SHAPE;
+    if (d->head_dim != 64 && d->head_dim != 128 && d->head_dim != 256) return SWATTN_ERR_SHAPE;
+    if (d->block_size < 1 || d->max_blocks_per_seq < 1 || d->num_blocks < 1 || d->max_ctx_len < 1)
+        return SWATTN_ERR_SHAPE;
+    if ((int64_t)d->max_ctx_len > (int64_t)d->max_blocks_per_seq * d->block_size)
+        return SWATTN_ERR_SHAPE;
+    if (n_q < 1 || n_q > SWATTN_MAX_NQ) return SWATTN_ERR_NQ;
+    if (window < 1) return SWATTN_ERR_WINDOW;
+    if (d->max_ctx_len < n_q) return SWATTN_ERR_CTX;
+    if (!dtype_in(d->q_dtype, {SWATTN_F32, SWATTN_BF16})) return SWATTN_ERR_DTYPE;
+    if (!dtype_in(d->kv_dtype, {SWATTN_F32, SWATTN_BF16, SWATTN_FP8_E4M3})) return SWATTN_ERR_DTYPE;
+    if (!dtype_in(d->out_dtype, {SWATTN_F32, SWATTN_BF16})) return SWATTN_ERR_DTYPE;
+    const bool fp8 = d->kv_dtype == SWATTN_FP8_E4M3;
+    if (fp8 && (!d->k_scale || !d->v_scale)) return SWATTN_ERR_DTYPE;
+    if (!fp8 && (d->k_scale || d->v_scale)) return SWATTN_ERR_DTYPE;
+    if (d->num_splits < 0) return SWATTN_ERR_ARG;
+    if (!dtype_in(d->variant, {SWATTN_VARIANT_AUTO, SWATTN_VARIANT_VALU, SWATTN_VARIANT_MFMA}))
+        return SWATTN_ERR_ARG;
+    if (d->variant == SWATTN_VARIANT_MFMA &&
+        (d->q_dtype != SWATTN_BF16 || d->kv_dtype == SWATTN_F32))
+        return SWATTN_ERR_DTYPE;
+    return SWATTN_OK;
+}
+
+swattn_status_t make_plan(const swattn_desc_t* d, int32_t n_q, int32_t window, swattn_plan_t* out) {
+    swattn_status_t st = validate_desc(d, n_q, window);
+    if (st != SWATTN_OK) return st;
+    if (!out) return SWATTN_ERR_NULL;
+
+    const int64_t G = d->num_heads / d->num_kv_heads;
+    const int64_t R = (int64_t)n_q * G;                       // query rows per (problem, KV head)
+    const int64_t D = d->head_dim;
+    const int64_t U = std::min<int64_t>(d->max_ctx_len, (int64_t)window + n_q - 1);  // union keys
+    const bool mfma_ok = d->q_dtype == SWATTN_BF16 && d->kv_dtype != SWATTN_F32;
+
+    int variant = d->variant;
+    if (variant == SWATTN_VARIANT_AUTO) variant = (mfma_ok && R >= 16) ? SWATTN_VARIANT_MFMA : SWATTN_VARIANT_VALU;
+
+    int64_t rows_per_chunk, S;
+    if (variant == SWATTN_VARIANT_MFMA) {
+        rows_per_chunk = R <= 32 ? 32 : (R <= 64 ? 64 : 128);
+        const int64_t row_chunks = (R + rows_per_chunk - 1) / rows_per_chunk;
+        const int64_t key_groups = 4 / (rows_per_chunk / kMfmaRowsPerWave);
+        const int64_t nch = (U + kMfmaChunkKeys - 1) / kMfmaChunkKeys + 1;   // +1: unaligned start
+        const int64_t units = (int64_t)d->batch * d->num_kv_heads * row_chunks;
+        const int64_t s_cap = std::max<int64_t>(1, (nch + key_groups - 1) / key_groups);
+        if (d->num_splits > 0)
+            S = clamp64(d->num_splits, 1, nch);
+        else
+            S = clamp64((kFillTarget + units - 1) / units, 1, s_cap);
+    } else {
+        rows_per_chunk = kValuRowsPerChunk;
+        const int64_t row_chunks = (R + rows_per_chunk - 1) / rows_per_chunk;
+        const int64_t units = (int64_t)d->batch * d->num_kv_heads * row_chunks;
+        const int64_t s_min = (U + kValuMaxKeys - 1) / kValuMaxKeys;
+        const int64_t s_cap = std::max<int64_t>(s_min, (U + kValuKeyRound - 1) / kValuKeyRound);
+        if (d->num_splits > 0)
+            S = clamp64(d->num_splits, s_min, U);
+        else
+            S = clamp64((kFillTarget + units - 1) / units, s_min, s_cap);
+    }
+    const int64_t row_chunks = (R + rows_per_chunk - 1) / rows_per_chunk;
+    const int64_t grid = (int64_t)d->batch * d->num_kv_heads * row_chunks * S;
+    if (grid > INT32_MAX) return SWATTN_ERR_SHAPE;
+
+    const int64_t rows_total = (int64_t)d->batch * d->num_kv_heads * R;
+    const int64_t merge_rows_per_wg = (kBlockThreads * 4) / D;   // D/4 threads per row
+    int64_t merge_grid = 0;
+    size_t ws = 0;
+    if (S > 1) {
+        merge_grid = (rows_total + merge_rows_per_wg - 1) / merge_rows_per_wg;
+        if (merge_grid > INT32_MAX) return SWATTN_ERR_SHAPE;
+        const int64_t o_bytes = ((rows_total * S * D * 4) + 255) / 256 * 256;
+        ws = (size_t)(o_bytes + rows_total * S * 4);
+    }
+    out->variant = variant;
+    out->num_splits = (int32_t)S;
+    out->rows_per_chunk = (int32_t)rows_per_chunk;
+    out->row_chunks = (int32_t)row_chunks;
+    out->grid = (int32_t)grid;
+    out->merge_grid = (int32_t)merge_grid;
+    out->workspace_bytes = ws;
+    return SWATTN_OK;
+}
+
+}  // namespace swattn
+
+extern "C" {
+
+swattn_status_t swattn_plan(const swattn_desc_t* desc, int32_t n_q, int32_t window, swattn_plan_t* plan) {
+    if (!plan) return SWATTN_ERR_NULL;
+    swattn_plan_t tmp;
+    swattn_status_t st = swattn::make_plan(desc, n_q, window, &tmp);
+    if (st == SWATTN_OK) *plan = tmp;
+    return st;
+}
+
+swattn_status_t swattn_workspace_bytes(const swattn_desc_t* desc, int32_t n_q, int32_t window, size_t* bytes) {
+    if (!bytes) return SWATTN_ERR_NULL;
+    swattn_plan_t tmp;
+    swattn_status_t st = swattn::make_plan(desc, n_q, window, &tmp);
+    if (st == SWATTN_OK) *bytes = tmp.workspace_bytes;
+    return st;
+}
+
+const char* swattn_status_str(swattn_status_t s) {
+    switch (s) {
+        case SWATTN_OK: return "ok";
+        case SWATTN_ERR_NULL: return "a required pointer is NULL";
+        case SWATTN_ERR_SHAPE: return "invalid shape (batch, heads, head_dim, block sizes or max_ctx_len)";
+        case SWATTN_ERR_NQ: return "n_q outside [1, 64]";
+        case SWATTN_ERR_WINDOW: return "window < 1";
+        case SWATTN_ERR_DTYPE: return "unsupported dtype combination (or e4m3 KV without scales, or scales without e4m3)";
+        case SWATTN_ERR_ALIGN: return "a data pointer is not 16-byte aligned";
+        case SWATTN_ERR_WORKSPACE: return "workspace missing or smaller than the plan needs";
+        case SWATTN_ERR_CTX: return "ctx_len outside [n_q, min(max_ctx_len, max_blocks_per_seq*block_size)]";
+        case SWATTN_ERR_BLOCK: return "a block id read by some window lies outside [0, num_blocks)";
+        case SWATTN_ERR_HIP: return "HIP runtime error";
+        case SWATTN_ERR_ARG: return "invalid argument";
+    }
+    return "unknown status";
+}
+
+int32_t swattn_abi_version(void) { return SWATTN_ABI_VERSION; }
+
+}  // extern "C"

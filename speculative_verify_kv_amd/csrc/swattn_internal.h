@@ -1,0 +1,55 @@
+// Internal interface between the host library (plan / api) and the kernels.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "swattn.h"
+
+namespace swattn {
+
+// Launch geometry shared by the planner and the kernels.
+constexpr int kWaveSize = 64;
+constexpr int kBlockThreads = 256;           // 4 waves per workgroup
+constexpr int kMfmaRowsPerWave = 32;         // two 16-row MFMA tiles
+constexpr int kMfmaChunkKeys = 32;           // keys per MFMA step (one 16x16x32 PV k-step)
+constexpr int kValuRowsPerChunk = 8;         // query rows per VALU workgroup
+constexpr int kValuMaxKeys = 256;            // keys per VALU workgroup (score buffer size)
+constexpr int kValuKeyRound = 64;            // keys scored per round in the VALU kernel
+
+// Everything a partition kernel needs, passed by value.
+struct PartitionParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const int32_t* block_table;
+    const int32_t* ctx_len;
+    const float* k_scale;
+    const float* v_scale;
+    void* out;
+    float* ws_o;          // [B*Hkv][S][R][D] normalised partial outputs (S > 1)
+    float* ws_lse;        // [B*Hkv][S][R] log2-sum-exp of each partial (S > 1)
+    int32_t B, H, Hkv, G, D, bs, max_blocks, num_blocks;
+    int32_t n_q, window, R, max_ctx;
+    int32_t S, rows_per_chunk, row_chunks;
+    int32_t q_dtype, kv_dtype, out_dtype;
+    float scale_log2;     // scale * log2(e)
+};
+
+struct MergeParams {
+    const float* ws_o;
+    const float* ws_lse;
+    void* out;
+    int32_t B, H, Hkv, G, D, n_q, R, S;
+    int32_t out_dtype;
+};
+
+// Geometry helpers used by both the planner and the host launch code.
+inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Kernel launchers (defined in the .hip files).  They return a hipError_t as int.
+int launch_partition_mfma(const PartitionParams& p, int grid, void* stream);
+int launch_partition_valu(const PartitionParams& p, int grid, void* stream);
+int launch_merge(const MergeParams& p, int grid, void* stream);
+
+}  // namespace swattn

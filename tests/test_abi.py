@@ -1,0 +1,150 @@
+"""CPU tests of the C ABI: the library loads, exports what include/swattn.h
+declares, and the host-side planner / argument checks behave (no GPU needed:
+none of these calls reaches a kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import speculative_verify_kv_amd as sw
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "swattn.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(swattn_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_header_symbol():
+    names = header_functions()
+    assert names == sorted(sw.EXPORTED)
+    lib = sw.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+        assert callable(getattr(sw, n)), n      # binding uses the same names
+
+
+def test_abi_version_and_status_strings():
+    assert sw.swattn_abi_version() == 1
+    for code in sw.STATUS:
+        s = sw.swattn_status_str(code)
+        assert s and s != "unknown status"
+    assert sw.swattn_status_str(12345) == "unknown status"
+
+
+def desc(**kw):
+    d = sw.swattn_desc_t()
+    base = dict(batch=24, num_heads=8, num_kv_heads=2, head_dim=256, block_size=16,
+                max_blocks_per_seq=256, num_blocks=6144, max_ctx_len=4096,
+                q_dtype=sw.SWATTN_BF16, kv_dtype=sw.SWATTN_BF16, out_dtype=sw.SWATTN_BF16,
+                k_scale=None, v_scale=None, num_splits=0, variant=0)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(d, k, v)
+    return d
+
+
+def status(d, n_q=8, window=188):
+    st, _ = sw.swattn_plan(d, n_q, window, check=False)
+    return sw.STATUS[st]
+
+
+@pytest.mark.parametrize("kw,n_q,window,expect", [
+    (dict(batch=0), 8, 188, "SWATTN_ERR_SHAPE"),
+    (dict(num_heads=6, num_kv_heads=4), 8, 188, "SWATTN_ERR_SHAPE"),
+    (dict(head_dim=96), 8, 188, "SWATTN_ERR_SHAPE"),
+    (dict(head_dim=512), 8, 188, "SWATTN_ERR_SHAPE"),
+    (dict(block_size=0), 8, 188, "SWATTN_ERR_SHAPE"),
+    (dict(num_blocks=0), 8, 188, "SWATTN_ERR_SHAPE"),
+    (dict(max_ctx_len=4097), 8, 188, "SWATTN_ERR_SHAPE"),
+    (dict(), 0, 188, "SWATTN_ERR_NQ"),
+    (dict(), 65, 188, "SWATTN_ERR_NQ"),
+    (dict(), 8, 0, "SWATTN_ERR_WINDOW"),
+    (dict(max_ctx_len=7), 8, 188, "SWATTN_ERR_CTX"),
+    (dict(q_dtype=sw.SWATTN_FP8_E4M3), 8, 188, "SWATTN_ERR_DTYPE"),
+    (dict(out_dtype=sw.SWATTN_FP8_E4M3), 8, 188, "SWATTN_ERR_DTYPE"),
+    (dict(kv_dtype=7), 8, 188, "SWATTN_ERR_DTYPE"),
+    (dict(kv_dtype=sw.SWATTN_FP8_E4M3), 8, 188, "SWATTN_ERR_DTYPE"),          # no scales
+    (dict(k_scale=16, v_scale=32), 8, 188, "SWATTN_ERR_DTYPE"),               # scales without e4m3
+    (dict(variant=sw.SWATTN_VARIANT_MFMA, q_dtype=sw.SWATTN_F32), 8, 188, "SWATTN_ERR_DTYPE"),
+    (dict(variant=sw.SWATTN_VARIANT_MFMA, kv_dtype=sw.SWATTN_F32), 8, 188, "SWATTN_ERR_DTYPE"),
+    (dict(variant=9), 8, 188, "SWATTN_ERR_ARG"),
+    (dict(num_splits=-1), 8, 188, "SWATTN_ERR_ARG"),
+    (dict(), 8, 188, "SWATTN_OK"),
+    (dict(), 64, 188, "SWATTN_OK"),
+    (dict(), 1, 2 ** 31 - 1, "SWATTN_OK"),
+])
+def test_plan_validation(kw, n_q, window, expect):
+    assert status(desc(**kw), n_q, window) == expect
+
+
+def test_plan_null_pointers():
+    lib = sw.lib()
+    p = sw.swattn_plan_t()
+    assert lib.swattn_plan(None, 8, 188, ctypes.byref(p)) == -1
+    d = desc()
+    assert lib.swattn_plan(ctypes.byref(d), 8, 188, None) == -1
+    assert lib.swattn_workspace_bytes(ctypes.byref(d), 8, 188, None) == -1
+
+
+def test_plan_variants_and_workspace():
+    # verify step: 8 queries x GQA 4 = 32 rows -> matrix cores
+    p = sw.swattn_plan(desc(), 8, 188)
+    assert p.variant == sw.SWATTN_VARIANT_MFMA and p.rows_per_chunk == 32 and p.row_chunks == 1
+    assert p.grid == 24 * 2 * p.num_splits
+    R, D, units = 32, 256, 24 * 2
+    if p.num_splits > 1:
+        o_bytes = -(-(units * R * p.num_splits * D * 4) // 256) * 256
+        assert p.workspace_bytes == o_bytes + units * R * p.num_splits * 4
+        assert p.merge_grid == -(-(units * R) // (1024 // D))
+    assert sw.swattn_workspace_bytes(desc(), 8, 188) == p.workspace_bytes
+    # decode: 4 rows -> vector ALU
+    p = sw.swattn_plan(desc(), 1, 188)
+    assert p.variant == sw.SWATTN_VARIANT_VALU
+    # float32 data -> vector ALU whatever the row count
+    p = sw.swattn_plan(desc(q_dtype=sw.SWATTN_F32, kv_dtype=sw.SWATTN_F32), 64, 188)
+    assert p.variant == sw.SWATTN_VARIANT_VALU and p.row_chunks == 64 * 4 // 8
+    # 64 queries x 4 = 256 rows -> two 128-row chunks
+    p = sw.swattn_plan(desc(), 64, 188)
+    assert p.rows_per_chunk == 128 and p.row_chunks == 2
+    # forced split count is honoured (within the chunk count), S = 1 needs no workspace
+    p = sw.swattn_plan(desc(num_splits=1), 8, 188)
+    assert p.num_splits == 1 and p.workspace_bytes == 0 and p.merge_grid == 0
+    p = sw.swattn_plan(desc(num_splits=3), 8, 188)
+    assert p.num_splits == 3 and p.workspace_bytes > 0
+    p = sw.swattn_plan(desc(num_splits=1000), 8, 188)
+    assert p.num_splits == 195 // 32 + 2
+    # the VALU kernel holds at most 256 keys per workgroup
+    p = sw.swattn_plan(desc(variant=sw.SWATTN_VARIANT_VALU, num_splits=1, max_ctx_len=4096), 8, 4096)
+    assert p.num_splits == 16
+
+
+def test_verify_host_checks_return_before_launch():
+    lib = sw.lib()
+    d = desc(num_splits=2)
+    plan = sw.swattn_plan(d, 8, 188)
+    A = 1 << 20   # fake, aligned, never dereferenced: every call below fails on the host
+
+    def call(q=A, k=2 * A, v=3 * A, bt=4 * A, ctx=5 * A, n_q=8, window=188, scale=0.0625,
+             out=6 * A, ws=8 * A, wsb=None, dd=d):
+        wsb = plan.workspace_bytes if wsb is None else wsb
+        return sw.STATUS[lib.swattn_verify(ctypes.byref(dd), q, k, v, bt, ctx, n_q, window, scale,
+                                           out, ws, wsb, None)]
+
+    assert call(q=None) == "SWATTN_ERR_NULL"
+    assert call(out=None) == "SWATTN_ERR_NULL"
+    assert call(bt=None) == "SWATTN_ERR_NULL"
+    assert call(q=A + 8) == "SWATTN_ERR_ALIGN"
+    assert call(k=2 * A + 2) == "SWATTN_ERR_ALIGN"
+    assert call(ctx=5 * A + 2) == "SWATTN_ERR_ALIGN"
+    assert call(scale=float("nan")) == "SWATTN_ERR_ARG"
+    assert call(scale=float("inf")) == "SWATTN_ERR_ARG"
+    assert call(out=A + 16) == "SWATTN_ERR_ARG"                       # overlaps q
+    assert call(ws=None) == "SWATTN_ERR_WORKSPACE"
+    assert call(wsb=plan.workspace_bytes - 1) == "SWATTN_ERR_WORKSPACE"
+    assert call(n_q=65) == "SWATTN_ERR_NQ"
+    assert call(window=0) == "SWATTN_ERR_WINDOW"
+    assert lib.swattn_check_inputs(ctypes.byref(d), None, 5 * A, 8, 188, None) == -1

@@ -1,0 +1,248 @@
+"""GPU parity: libswattn (through its C ABI) against the float64 oracle.
+
+Every case compares the HIP output element by element with ``oracle.attend`` on
+the same seeded inputs, at the tolerance stated in tests/gpu_util.py.  The named
+workloads run at full size in the launch configuration the bench times.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import speculative_verify_kv_amd as sw
+import synth
+import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+NAMED = list(synth.NAMED)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    sw.lib()
+
+
+# ---------------------------------------------------------------------------
+# the named workloads, full size, default plan
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("key", NAMED)
+def test_named_workload(key):
+    gu.log(f"[named] {key}")
+    w, ref = gu.named(key)
+    got, plan = gu.run(w)
+    gu.log(f"  plan {plan.as_dict()}")
+    gu.check(got, ref, w.kv_dtype, out_f32=(w.q_dtype == "f32"), label=key)
+
+
+@pytest.mark.parametrize("key", ["verify", "wide_verify", "batched_fp8", "fullctx_2048"])
+def test_named_workload_f32_out(key):
+    gu.log(f"[named f32 out] {key}")
+    w, ref = gu.named(key)
+    got, _ = gu.run(w, out_f32=True)
+    gu.check(got, ref, w.kv_dtype, out_f32=True, label=key + "/f32")
+
+
+# ---------------------------------------------------------------------------
+# split-count invariance and run-to-run determinism
+# ---------------------------------------------------------------------------
+def test_split_invariance_and_determinism_mfma():
+    w, ref = gu.named("verify")
+    t = gu.upload(w)
+    outs = {}
+    for S in (1, 2, 3, 4, 7):
+        gu.log(f"[splits] S={S}")
+        got, plan = gu.run(w, t, out_f32=True, num_splits=S)
+        assert plan.num_splits == S and plan.variant == sw.SWATTN_VARIANT_MFMA
+        gu.check(got, ref, w.kv_dtype, True, label=f"verify S={S}")
+        again, _ = gu.run(w, t, out_f32=True, num_splits=S)
+        assert np.array_equal(got, again), f"S={S} not bitwise deterministic"
+        outs[S] = got
+    for S in outs:
+        assert np.abs(outs[S] - outs[1]).max() <= 2e-3
+
+
+def test_split_invariance_valu_decode():
+    w = synth.make_workload("decode", B=6, H=8, Hkv=2, D=256, n_q=1, window=188, ctx=[300, 188, 1, 4096, 189, 2000],
+                            bs=16, seed=5, recent=188, max_blocks=256)
+    ref = gu.reference(w)
+    t = gu.upload(w)
+    for S in (1, 2, 3):
+        gu.log(f"[valu splits] S={S}")
+        got, plan = gu.run(w, t, out_f32=True, num_splits=S, max_ctx=4096)
+        assert plan.variant == sw.SWATTN_VARIANT_VALU and plan.num_splits == S
+        gu.check(got, ref, w.kv_dtype, True, label=f"decode S={S}")
+
+
+def test_variants_agree():
+    w = synth.make_workload("verify_small", B=4, H=8, Hkv=2, D=256, n_q=8, window=188, ctx=[4096, 200, 8, 1000],
+                            bs=16, seed=6, max_blocks=256)
+    ref = gu.reference(w)
+    t = gu.upload(w)
+    for variant in (sw.SWATTN_VARIANT_VALU, sw.SWATTN_VARIANT_MFMA):
+        gu.log(f"[variant] {variant}")
+        got, plan = gu.run(w, t, out_f32=True, variant=variant, max_ctx=4096)
+        assert plan.variant == variant
+        gu.check(got, ref, w.kv_dtype, True, label=f"variant {variant}")
+
+
+# ---------------------------------------------------------------------------
+# randomised shapes
+# ---------------------------------------------------------------------------
+DTYPES = [("bf16", "bf16"), ("bf16", "e4m3"), ("f32", "f32"), ("bf16", "f32"), ("f32", "bf16")]
+
+
+def fuzz_cases(n=48, seed=1234):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for k in range(n):
+        n_q = int(rng.choice([1, 2, 3, 7, 8, 16, 33, 64]))
+        window = int(rng.choice([1, 2, 15, 16, 17, 188, 4096]))
+        bs = int(rng.choice([1, 16, 300]))
+        G = int(rng.choice([1, 2, 4, 8]))
+        Hkv = int(rng.choice([1, 2]))
+        D = int(rng.choice([64, 128, 256]))
+        qd, kd = DTYPES[k % len(DTYPES)]
+        B = int(rng.choice([1, 3]))
+        ctx = [int(rng.integers(n_q, 700)) for _ in range(B)]
+        out_f32 = bool(rng.integers(0, 2))
+        S = int(rng.choice([0, 0, 1, 2, 5]))
+        sentinels = bool(rng.integers(0, 2))
+        cases.append(dict(idx=k, n_q=n_q, window=window, bs=bs, G=G, Hkv=Hkv, D=D, qd=qd, kd=kd,
+                          B=B, ctx=ctx, out_f32=out_f32, S=S, sentinels=sentinels))
+    return cases
+
+
+@pytest.mark.parametrize("case", fuzz_cases(), ids=lambda c: f"fz{c['idx']}")
+def test_fuzz(case):
+    c = case
+    gu.log(f"[fuzz] {c}")
+    w = synth.make_workload(f"fz{c['idx']}", B=c["B"], H=c["G"] * c["Hkv"], Hkv=c["Hkv"], D=c["D"],
+                            n_q=c["n_q"], window=c["window"], ctx=c["ctx"], bs=c["bs"],
+                            seed=100 + c["idx"], q_dtype=c["qd"], kv_dtype=c["kd"],
+                            recent=(c["window"] + c["n_q"] - 1) if c["sentinels"] else None)
+    ref = gu.reference(w)
+    got, plan = gu.run(w, out_f32=c["out_f32"] or c["qd"] == "f32", num_splits=c["S"])
+    gu.log(f"  plan {plan.as_dict()}")
+    gu.check(got, ref, w.kv_dtype, c["out_f32"] or c["qd"] == "f32", label=f"fz{c['idx']}")
+
+
+# ---------------------------------------------------------------------------
+# mask pattern: one-hot V rows turn the output into the softmax weights
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("variant", [sw.SWATTN_VARIANT_MFMA, sw.SWATTN_VARIANT_VALU])
+def test_one_hot_values_expose_mask(variant):
+    gu.log(f"[one-hot] variant {variant}")
+    w = synth.make_workload("onehot", B=3, H=8, Hkv=2, D=256, n_q=8, window=188, ctx=[4096, 300, 195],
+                            bs=16, seed=7, recent=195, max_blocks=256)
+    lo, hi = oracle.window_bounds(w.ctx_len, w.n_q, w.window)
+    one = synth.to_bf16_bits(np.float32([1.0]))[0]
+    for b in range(w.B):
+        u_lo = int(lo[b, 0])
+        for j in range(u_lo, int(hi[b, -1]) + 1):
+            blk = w.block_table[b, j // w.bs]
+            w.v_cache[blk, :, j % w.bs, :] = 0
+            w.v_cache[blk, :, j % w.bs, j - u_lo] = one
+    _, weights = oracle.attend(w.q, w.k_cache, w.v_cache, w.block_table, w.ctx_len, w.n_q, w.window,
+                               w.scale, q_format="bf16", kv_format="bf16", return_weights=True)
+    got, _ = gu.run(w, out_f32=True, variant=variant)
+    for b in range(w.B):
+        u_lo, u_hi = int(lo[b, 0]), int(hi[b, -1])
+        n = u_hi - u_lo + 1
+        wref = weights[b, :, :, u_lo:u_hi + 1]                 # [n_q, H, n]
+        g = got[b, :, :, :n]
+        assert ((g == 0.0) == (wref == 0.0)).all(), "zero pattern differs from the window mask"
+        assert (got[b, :, :, n:] == 0.0).all()
+        np.testing.assert_allclose(g, wref, rtol=0, atol=2e-3)
+
+
+def test_window_one_returns_own_value_row_exactly():
+    w = synth.make_workload("w1", B=2, H=8, Hkv=2, D=128, n_q=8, window=1, ctx=[40, 17], bs=16, seed=8)
+    for variant, out_f32 in ((sw.SWATTN_VARIANT_MFMA, False), (sw.SWATTN_VARIANT_MFMA, True),
+                             (sw.SWATTN_VARIANT_VALU, True)):
+        got, _ = gu.run(w, out_f32=out_f32, variant=variant)
+        for b in range(w.B):
+            for i in range(w.n_q):
+                pos = int(w.ctx_len[b]) - w.n_q + i
+                for h in range(w.H):
+                    bits = w.v_cache[w.block_table[b, pos // w.bs], h // 4, pos % w.bs]
+                    row = (bits.astype(np.uint32) << 16).view(np.float32)
+                    assert np.array_equal(got[b, i, h], row)
+
+
+def test_edge_shapes():
+    cases = [
+        dict(B=1, H=2, Hkv=1, D=64, n_q=1, window=1, ctx=[1], bs=1),          # one position
+        dict(B=2, H=8, Hkv=1, D=64, n_q=64, window=2 ** 31 - 1, ctx=[64, 70], bs=16),   # huge window, p = 0
+        dict(B=1, H=16, Hkv=2, D=128, n_q=64, window=188, ctx=[4096], bs=16),  # 512 rows, 4 row chunks
+        dict(B=2, H=4, Hkv=4, D=256, n_q=5, window=3, ctx=[5, 600], bs=300),   # G = 1, big blocks
+    ]
+    for k, c in enumerate(cases):
+        gu.log(f"[edge] {c}")
+        w = synth.make_workload(f"edge{k}", seed=20 + k, **c)
+        ref = gu.reference(w)
+        got, plan = gu.run(w, out_f32=True)
+        gu.log(f"  plan {plan.as_dict()}")
+        gu.check(got, ref, w.kv_dtype, True, label=f"edge{k}")
+
+
+# ---------------------------------------------------------------------------
+# bad device-resident inputs are turned into NaN by the kernels' own checks
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("variant", [sw.SWATTN_VARIANT_MFMA, sw.SWATTN_VARIANT_VALU])
+def test_bad_ctx_and_block_ids_give_nan(variant):
+    w = synth.make_workload("bad", B=4, H=8, Hkv=2, D=128, n_q=8, window=188, ctx=[300, 300, 300, 300],
+                            bs=16, seed=9)
+    ref = gu.reference(w)
+    w.ctx_len[1] = 7                                   # < n_q
+    w.ctx_len[2] = 1000                                # > max_blocks * bs (and > max_ctx_len)
+    w.block_table[3, 299 // 16] = w.num_blocks + 5     # block id out of range inside the window
+    t = gu.upload(w)
+    desc = sw.make_desc(t["q"], t["k"], t["bt"], 300)
+    assert sw.STATUS[sw.swattn_check_inputs(desc, t["bt"], t["ctx"], 8, 188)] == "SWATTN_ERR_CTX"
+    out, _ = sw.verify(t["q"], t["k"], t["v"], t["bt"], t["ctx"], 8, 188, w.scale, max_ctx_len=300,
+                       out_dtype=sw.SWATTN_F32, variant=variant)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    gu.check(got[0:1], ref[0:1], w.kv_dtype, True, label="good sequence")
+    assert np.isnan(got[1]).all() and np.isnan(got[2]).all()
+    assert np.isnan(got[3]).any()
+
+
+def test_check_inputs_reports_block_errors():
+    w = synth.make_workload("chk", B=2, H=8, Hkv=2, D=64, n_q=8, window=188, ctx=[300, 100], bs=16, seed=10)
+    t = gu.upload(w)
+    desc = sw.make_desc(t["q"], t["k"], t["bt"], 300)
+    assert sw.swattn_check_inputs(desc, t["bt"], t["ctx"], 8, 188) == 0
+    t["bt"][1, 3] = -1
+    assert sw.STATUS[sw.swattn_check_inputs(desc, t["bt"], t["ctx"], 8, 188)] == "SWATTN_ERR_BLOCK"
+
+
+# ---------------------------------------------------------------------------
+# HIP graph capture and replay
+# ---------------------------------------------------------------------------
+def test_graph_capture_replay():
+    w, ref = gu.named("verify")
+    t = gu.upload(w)
+    desc = sw.make_desc(t["q"], t["k"], t["bt"], 4096, num_splits=2)
+    plan = sw.swattn_plan(desc, w.n_q, w.window)
+    out = torch.empty(t["q"].shape, dtype=torch.bfloat16, device=gu.DEV)
+    ws = torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device=gu.DEV)
+    sw.verify(t["q"], t["k"], t["v"], t["bt"], t["ctx"], w.n_q, w.window, w.scale, 4096,
+              out=out, num_splits=2, workspace=ws)
+    torch.cuda.synchronize()
+    eager = out.clone()
+    out.zero_()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        sw.verify(t["q"], t["k"], t["v"], t["bt"], t["ctx"], w.n_q, w.window, w.scale, 4096,
+                  out=out, num_splits=2, workspace=ws)
+    for rep in range(4):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {rep} differs from eager"
+    gu.check(eager.float().cpu().numpy().astype(np.float64), ref, w.kv_dtype, False, label="graph")
