@@ -35,6 +35,16 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 WORKLOAD = "verify"
+DESCRIPTIONS = {
+    "verify": "single-stream verify: 24 layers x (8 q heads / 2 kv heads), head_dim 256, bf16, "
+              "ctx 4096, window 188, n_q 8, paged block 16 (shuffled), seed 1",
+    "batched_fp8": "batched stress: 256 sequences x (8 q heads / 2 kv heads), head_dim 256, e4m3 KV "
+                   "(per-head scale), bf16 Q/out, ctx ~ U[188, 4096], window 188, n_q 8, block 16, seed 4",
+    "batched_bf16": "batched stress: 256 sequences x (8 q / 2 kv heads), head_dim 256, bf16, "
+                    "ctx ~ U[188, 4096], window 188, n_q 8, block 16, seed 4",
+    "wide_verify": "wide verify: 24 layers x (8 q / 2 kv heads), head_dim 256, bf16, ctx 4096, window 188, "
+                   "n_q 64, 5% of Q rows x8, block 16, seed 3",
+}
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_verify_24x2kv_d256_w188_nq8.txt")
 KERNEL_SOURCES = ["partition_mfma.hip", "partition_valu.hip", "merge.hip", "kv_access.h",
                   "swattn_internal.h", "plan.cpp", "api.cpp"]
@@ -111,6 +121,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--splits", type=int, default=0, help="force the KV split count (0 = library)")
+    ap.add_argument("--workload", default=WORKLOAD, help="named synthetic workload (default: verify)")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
@@ -141,20 +152,24 @@ def main():
         print(json.dumps({"calibrate_copy_bytes": n}))
         return
 
-    w = synth.named_workload(WORKLOAD)
+    w = synth.named_workload(args.workload)
 
-    def to_dev_bf16(a):
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    def to_dev(a, fmt):
+        if fmt == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
-    q = to_dev_bf16(w.q)
-    k = to_dev_bf16(w.k_cache)
-    v = to_dev_bf16(w.v_cache)
+    q = to_dev(w.q, w.q_dtype)
+    k = to_dev(w.k_cache, w.kv_dtype)
+    v = to_dev(w.v_cache, w.kv_dtype)
+    ks = None if w.k_scale is None else torch.from_numpy(w.k_scale).to(dev)
+    vs = None if w.v_scale is None else torch.from_numpy(w.v_scale).to(dev)
     bt = torch.from_numpy(w.block_table).to(dev)
     ctx = torch.from_numpy(w.ctx_len).to(dev)
     max_ctx = int(w.ctx_len.max())
-    desc = sw.make_desc(q, k, bt, max_ctx, num_splits=args.splits)
+    desc = sw.make_desc(q, k, bt, max_ctx, k_scale=ks, v_scale=vs, num_splits=args.splits)
     plan = sw.swattn_plan(desc, w.n_q, w.window)
-    out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    out = torch.empty(q.shape, dtype=torch.float32 if w.q_dtype == "f32" else torch.bfloat16, device=dev)
     ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
@@ -177,9 +192,10 @@ def main():
     for b in rng.choice(w.B, size=3, replace=False):
         sub = dict(q=w.q[b:b + 1], block_table=w.block_table[b:b + 1], ctx_len=w.ctx_len[b:b + 1])
         ref = oracle.attend(sub["q"], w.k_cache, w.v_cache, sub["block_table"], sub["ctx_len"], w.n_q,
-                            w.window, w.scale, q_format="bf16", kv_format="bf16")
+                            w.window, w.scale, q_format=w.q_format, kv_format=w.kv_format,
+                            k_scale=w.k_scale, v_scale=w.v_scale)
         worst = max(worst, float((np.abs(got[b:b + 1] - ref) - 1e-2 * np.abs(ref)).max()))
-    parity_ok = worst <= 2e-3
+    parity_ok = worst <= (2e-2 if w.kv_dtype == "e4m3" else 2e-3)
 
     # ---- cold-cache timed region ------------------------------------------------------
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
@@ -240,11 +256,10 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": w.kv_dtype if w.kv_dtype != w.q_dtype else w.q_dtype,
         "data": "synthetic",
         "config": {
-            "workload": "single-stream verify: 24 layers x (8 q heads / 2 kv heads), head_dim 256, "
-                        "bf16, ctx 4096, window 188, n_q 8, paged block 16 (shuffled), seed 1",
+            "workload": DESCRIPTIONS.get(args.workload, w.name),
             "global_batch": w.B, "seq_len": int(max_ctx), "parallelism": "none (1 GPU)",
         },
         "roofline": {

@@ -23,35 +23,26 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
 }
 
-// OCP E4M3 code -> its value times 2^-8, exactly.
-//
-// The 7 magnitude bits of an E4M3 code, shifted left by 7, form an IEEE half
-// whose exponent field is the E4M3 exponent field and whose top 3 mantissa bits
-// are the E4M3 mantissa: the half's value is the E4M3 value times 2^(7-15), for
-// normals and subnormals alike (both formats keep subnormals).  The half -> float
-// conversion is exact.  The two NaN codes (magnitude 0x7F) map to NaN.  Callers
-// multiply the 2^8 back in through their per-head scale.
-__device__ __forceinline__ float e4m3_to_f32_div256(uint32_t code) {
-    const uint32_t mag = code & 0x7Fu;
-    const uint16_t hbits = (uint16_t)(((code & 0x80u) << 8) | (mag << 7));
-    const float f = (float)__builtin_bit_cast(_Float16, hbits);
-    return mag == 0x7Fu ? __builtin_nanf("") : f;
+// OCP E4M3 -> float, exactly, with gfx950's conversion instruction
+// (v_cvt_pk_f32_fp8 decodes the OCP E4M3 format on this target: bias 7,
+// subnormals kept, S.1111.111 is NaN).  `hi` selects bytes 2-3 instead of 0-1.
+__device__ __forceinline__ void e4m3x2_to_f32(uint32_t word, bool hi, float& a, float& b) {
+    const auto v = hi ? __builtin_amdgcn_cvt_pk_f32_fp8(word, true) : __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
+    a = v[0];
+    b = v[1];
 }
 
-// 8 E4M3 codes (little-endian in a uint2) -> 8 bfloat16 values (times 2^-8), exact:
-// an E4M3 value has at most 4 significant bits, so truncating its float to bf16 is exact.
-__device__ __forceinline__ uint4 e4m3x8_to_bf16x8_div256(uint2 w) {
-    uint4 r;
-    uint32_t* o = reinterpret_cast<uint32_t*>(&r);
+// 8 E4M3 codes (little-endian in a uint2) -> 8 bfloat16 values, exactly: an E4M3
+// value has at most 4 significant bits, so keeping the upper half of its float is exact.
+__device__ __forceinline__ uint4 e4m3x8_to_bf16x8(uint2 w) {
+    uint32_t o[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        const uint32_t word = k < 2 ? w.x : w.y;
-        const int sh = (k & 1) * 16;
-        const float lo = e4m3_to_f32_div256((word >> sh) & 0xFFu);
-        const float hi = e4m3_to_f32_div256((word >> (sh + 8)) & 0xFFu);
-        o[k] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+        float a, b;
+        e4m3x2_to_f32(k < 2 ? w.x : w.y, (k & 1) != 0, a, b);
+        o[k] = (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xFFFF0000u);
     }
-    return r;
+    return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
 __device__ __forceinline__ uint4 ld_global_16(const void* p) {

@@ -28,7 +28,6 @@ namespace {
 enum { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2 };
 
 // N consecutive cached elements starting at element offset `off` -> float.
-// For e4m3 the values come out times 2^-8 (the caller's scale carries 2^8).
 template <int KVT, int N>
 __device__ __forceinline__ void load_kv(const void* base, int64_t off, float* dst) {
     if constexpr (KVT == KV_F32) {
@@ -67,13 +66,13 @@ __device__ __forceinline__ void load_kv(const void* base, int64_t off, float* ds
                 const uint4 v = ld_global_16(src + k);
                 const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-                for (int e = 0; e < 16; ++e) dst[k + e] = e4m3_to_f32_div256((w[e >> 2] >> (8 * (e & 3))) & 0xFFu);
+                for (int e = 0; e < 16; e += 2) e4m3x2_to_f32(w[e >> 2], (e & 2) != 0, dst[k + e], dst[k + e + 1]);
             }
         } else {
             static_assert(N == 4, "e4m3 loads of 4 or a multiple of 16");
             const uint32_t w = *reinterpret_cast<const uint32_t*>(src);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) dst[e] = e4m3_to_f32_div256((w >> (8 * e)) & 0xFFu);
+            e4m3x2_to_f32(w, false, dst[0], dst[1]);
+            e4m3x2_to_f32(w, true, dst[2], dst[3]);
         }
     }
 }
@@ -127,8 +126,8 @@ __global__ __launch_bounds__(kBlockThreads) void partition_valu_kernel(Partition
     float sl2 = p.scale_log2;
     float osc = 1.0f;
     if constexpr (KVT == KV_FP8) {
-        sl2 *= p.k_scale[g] * 256.0f;
-        osc = p.v_scale[g] * 256.0f;
+        sl2 *= p.k_scale[g];
+        osc = p.v_scale[g];
     }
 
     // ---- Q rows of this chunk -> LDS (float) ---------------------------------------

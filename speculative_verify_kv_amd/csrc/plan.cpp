@@ -36,6 +36,9 @@ swattn_status_t validate_desc(const swattn_desc_t* d, int32_t n_q, int32_t windo
         return SWATTN_ERR_SHAPE;
     if ((int64_t)d->max_ctx_len > (int64_t)d->max_blocks_per_seq * d->block_size)
         return SWATTN_ERR_SHAPE;
+    // cache rows are indexed with 32-bit integers inside the kernels
+    if ((int64_t)d->num_blocks * d->num_kv_heads * d->block_size > INT32_MAX) return SWATTN_ERR_SHAPE;
+    if ((int64_t)d->max_blocks_per_seq * d->block_size > INT32_MAX) return SWATTN_ERR_SHAPE;
     if (n_q < 1 || n_q > SWATTN_MAX_NQ) return SWATTN_ERR_NQ;
     if (window < 1) return SWATTN_ERR_WINDOW;
     if (d->max_ctx_len < n_q) return SWATTN_ERR_CTX;
@@ -70,16 +73,12 @@ swattn_status_t make_plan(const swattn_desc_t* d, int32_t n_q, int32_t window, s
 
     int64_t rows_per_chunk, S;
     if (variant == SWATTN_VARIANT_MFMA) {
-        rows_per_chunk = R <= 32 ? 32 : (R <= 64 ? 64 : 128);
-        const int64_t row_chunks = (R + rows_per_chunk - 1) / rows_per_chunk;
-        const int64_t key_groups = 4 / (rows_per_chunk / kMfmaRowsPerWave);
-        const int64_t nch = (U + kMfmaChunkKeys - 1) / kMfmaChunkKeys + 1;   // +1: unaligned start
-        const int64_t units = (int64_t)d->batch * d->num_kv_heads * row_chunks;
-        const int64_t s_cap = std::max<int64_t>(1, (nch + key_groups - 1) / key_groups);
+        rows_per_chunk = kMfmaRows;
+        const int64_t s_min = (U + kMfmaMaxKeys - 1) / kMfmaMaxKeys;
         if (d->num_splits > 0)
-            S = clamp64(d->num_splits, 1, nch);
+            S = clamp64(d->num_splits, s_min, std::max<int64_t>(s_min, (U + 15) / 16));
         else
-            S = clamp64((kFillTarget + units - 1) / units, 1, s_cap);
+            S = s_min;
     } else {
         rows_per_chunk = kValuRowsPerChunk;
         const int64_t row_chunks = (R + rows_per_chunk - 1) / rows_per_chunk;

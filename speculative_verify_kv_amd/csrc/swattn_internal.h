@@ -10,9 +10,11 @@ namespace swattn {
 
 // Launch geometry shared by the planner and the kernels.
 constexpr int kWaveSize = 64;
-constexpr int kBlockThreads = 256;           // 4 waves per workgroup
-constexpr int kMfmaRowsPerWave = 32;         // two 16-row MFMA tiles
-constexpr int kMfmaChunkKeys = 32;           // keys per MFMA step (one 16x16x32 PV k-step)
+constexpr int kBlockThreads = 256;           // 4 waves: VALU partition and merge kernels
+constexpr int kMfmaThreads = 256;            // 4 waves: matrix-core partition kernel
+constexpr int kMfmaRows = 32;                // query rows per matrix-core workgroup (two 16-row tiles)
+constexpr int kMfmaTileKeys = 64;            // keys per online-softmax step (16 per wave)
+constexpr int kMfmaMaxKeys = 512;            // keys per matrix-core workgroup (cache-row table in LDS)
 constexpr int kValuRowsPerChunk = 8;         // query rows per VALU workgroup
 constexpr int kValuMaxKeys = 256;            // keys per VALU workgroup (score buffer size)
 constexpr int kValuKeyRound = 64;            // keys scored per round in the VALU kernel

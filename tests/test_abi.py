@@ -107,16 +107,19 @@ def test_plan_variants_and_workspace():
     # float32 data -> vector ALU whatever the row count
     p = sw.swattn_plan(desc(q_dtype=sw.SWATTN_F32, kv_dtype=sw.SWATTN_F32), 64, 188)
     assert p.variant == sw.SWATTN_VARIANT_VALU and p.row_chunks == 64 * 4 // 8
-    # 64 queries x 4 = 256 rows -> two 128-row chunks
+    # 64 queries x 4 = 256 rows -> eight 32-row chunks
     p = sw.swattn_plan(desc(), 64, 188)
-    assert p.rows_per_chunk == 128 and p.row_chunks == 2
+    assert p.rows_per_chunk == 32 and p.row_chunks == 8
     # forced split count is honoured (within the chunk count), S = 1 needs no workspace
     p = sw.swattn_plan(desc(num_splits=1), 8, 188)
     assert p.num_splits == 1 and p.workspace_bytes == 0 and p.merge_grid == 0
     p = sw.swattn_plan(desc(num_splits=3), 8, 188)
     assert p.num_splits == 3 and p.workspace_bytes > 0
     p = sw.swattn_plan(desc(num_splits=1000), 8, 188)
-    assert p.num_splits == 195 // 32 + 2
+    assert p.num_splits == -(-195 // 16)                 # at most one split per 16 keys
+    # the matrix-core kernel holds at most 512 keys per workgroup
+    p = sw.swattn_plan(desc(num_splits=1), 8, 4096)
+    assert p.variant == sw.SWATTN_VARIANT_MFMA and p.num_splits == 8
     # the VALU kernel holds at most 256 keys per workgroup
     p = sw.swattn_plan(desc(variant=sw.SWATTN_VARIANT_VALU, num_splits=1, max_ctx_len=4096), 8, 4096)
     assert p.num_splits == 16

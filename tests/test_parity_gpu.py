@@ -246,3 +246,23 @@ def test_graph_capture_replay():
         torch.cuda.synchronize()
         assert torch.equal(out, eager), f"replay {rep} differs from eager"
     gu.check(eager.float().cpu().numpy().astype(np.float64), ref, w.kv_dtype, False, label="graph")
+
+
+# ---------------------------------------------------------------------------
+# every e4m3 code decodes exactly: window 1 returns the query's own V row
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("variant", [sw.SWATTN_VARIANT_MFMA, sw.SWATTN_VARIANT_VALU])
+def test_e4m3_every_code_through_window_one(variant):
+    from oracle.formats import e4m3_value_table
+    w = synth.make_workload("codes", B=1, H=4, Hkv=1, D=256, n_q=2, window=1, ctx=[37], bs=16, seed=11,
+                            kv_dtype="e4m3")
+    pos = int(w.ctx_len[0]) - 1                       # the last query's own position
+    blk = w.block_table[0, pos // w.bs]
+    w.v_cache[blk, 0, pos % w.bs, :] = np.arange(256, dtype=np.uint8)
+    w.v_scale[:] = 1.0
+    got, _ = gu.run(w, out_f32=True, variant=variant)
+    table = e4m3_value_table()
+    for h in range(w.H):
+        row = got[0, 1, h]
+        assert np.array_equal(np.isnan(row), np.isnan(table))
+        assert np.array_equal(row[~np.isnan(table)], table[~np.isnan(table)])
