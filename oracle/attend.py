@@ -3,7 +3,7 @@
 TEST INFRASTRUCTURE ONLY (see oracle/__init__.py).
 
 Semantics (from "The Fast Gemma Challenge: our verified-SOTA recipe, in full",
-manifest and "What each piece does, and why"; readings listed in the design doc):
+manifest and "What each piece does, and why"):
 
 * One verify step scores ``n_q`` new positions of a sequence: the target token
   plus the MTP drafts (manifest ``SPECULATIVE_CONFIG``: 7 drafts, so n_q = 8;
