@@ -76,6 +76,9 @@ extern "C" swattn_status_t swattn_verify(const swattn_desc_t* d, const void* q, 
     p.G = (int32_t)G;
     p.D = d->head_dim;
     p.bs = d->block_size;
+    p.bs_log2 = -1;
+    for (int k = 0; k < 31; ++k)
+        if (d->block_size == (1 << k)) p.bs_log2 = k;
     p.max_blocks = d->max_blocks_per_seq;
     p.num_blocks = d->num_blocks;
     p.n_q = n_q;

@@ -7,8 +7,8 @@
 // 64 with an online softmax; within a tile:
 //
 //   phase A  wave w scores keys 16w..16w+15 of the tile for all 32 rows:
-//            S^T = K . Q^T, K rows straight from HBM as the A operand, Q^T held
-//            in registers.  The window mask (t - W, t] and the softmax scale are
+//            S^T = K . Q^T, K rows straight from HBM as the A operand, Q^T read
+//            from the workgroup's Q rows in LDS.  The window mask (t - W, t] and the softmax scale are
 //            applied and S goes to LDS; the wave also stages V of its 16 keys
 //            into LDS transposed (V^T[d][key]), then issues the loads of its
 //            next tile so they overlap the rest of this one.
@@ -42,12 +42,13 @@ constexpr int kSStride = kT + 4;            // floats per S row (272 B); P hi/lo
 template <int D>
 struct MfmaLds {
     static constexpr int kVtBytes = D * kVtStride * 2;
-    static constexpr int kQStride = D + 8;  // bf16 per staged Q row (aliases the V^T area)
+    static constexpr int kQStride = D + 8;  // bf16 per staged Q row
+    static constexpr int kQBytes = kMfmaRows * kQStride * 2;
     static constexpr int kSBytes = kMfmaRows * kSStride * 4;
     static constexpr int kRowIdxBytes = kMfmaMaxKeys * 4;
     static constexpr int kMiscBytes = 3 * kMfmaRows * 4;   // alpha, final max, final sum
-    static constexpr int kBytes = kVtBytes + kSBytes + kRowIdxBytes + kMiscBytes;
-    static_assert(kMfmaRows * kQStride * 2 <= kVtBytes, "Q staging must fit in the V^T area");
+    static constexpr int kTableBytes = kMfmaThreads * 4;   // block-table row (short rows only)
+    static constexpr int kBytes = kVtBytes + kQBytes + kSBytes + kRowIdxBytes + kMiscBytes + kTableBytes;
 };
 
 __device__ __forceinline__ f32x4_t mfma_bf16(uint4 a, uint4 b, f32x4_t c) {
@@ -93,12 +94,13 @@ __global__ __launch_bounds__(kMfmaThreads) void partition_mfma_kernel(PartitionP
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[L::kBytes];
     uint16_t* vt = reinterpret_cast<uint16_t*>(smem);
-    uint16_t* qs = reinterpret_cast<uint16_t*>(smem);                 // Q staging, before any V^T
-    float* sbuf = reinterpret_cast<float*>(smem + L::kVtBytes);
-    int* rowidx = reinterpret_cast<int*>(smem + L::kVtBytes + L::kSBytes);
+    uint16_t* qs = reinterpret_cast<uint16_t*>(smem + L::kVtBytes);    // Q rows, read as Q^T operands
+    float* sbuf = reinterpret_cast<float*>(smem + L::kVtBytes + L::kQBytes);
+    int* rowidx = reinterpret_cast<int*>(smem + L::kVtBytes + L::kQBytes + L::kSBytes);
     float* alpha_s = reinterpret_cast<float*>(rowidx + kMfmaMaxKeys);
     float* st_m = alpha_s + kMfmaRows;
     float* st_l = st_m + kMfmaRows;
+    int* tbl = reinterpret_cast<int*>(st_l + kMfmaRows);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -114,6 +116,10 @@ __global__ __launch_bounds__(kMfmaThreads) void partition_mfma_kernel(PartitionP
     const int g = lin % p.Hkv;
     const int b = lin / p.Hkv;
 
+    // A block-table row that fits one entry per thread is read while ctx_len is in
+    // flight, which removes one dependent round trip to memory.
+    const bool short_row = p.max_blocks <= kMfmaThreads;
+    const int tb = (short_row && tid < p.max_blocks) ? p.block_table[(int64_t)b * p.max_blocks + tid] : 0;
     const int ctx = p.ctx_len[b];
     const bool seq_ok = ctx >= p.n_q && ctx <= p.max_blocks * p.bs && ctx <= p.max_ctx;
     const int pos0 = seq_ok ? ctx - p.n_q : 0;             // position of query 0
@@ -126,14 +132,19 @@ __global__ __launch_bounds__(kMfmaThreads) void partition_mfma_kernel(PartitionP
     }
     const int ntiles = (nk + kT - 1) / kT;
 
+    if (short_row) {
+        tbl[tid] = tb;
+        __syncthreads();
+    }
+
     // ---- key -> cache row (phys * Hkv + g) * bs + off; -1 bad block id, -2 no key -----
     for (int t = tid; t < kMfmaMaxKeys; t += kMfmaThreads) {
         int ri = -2;
         if (t < nk) {
             const int j = k0 + t;
-            const int blk = j / p.bs;
+            const int blk = p.bs_log2 >= 0 ? j >> p.bs_log2 : j / p.bs;
             const int off = j - blk * p.bs;
-            const int phys = p.block_table[(int64_t)b * p.max_blocks + blk];
+            const int phys = short_row ? tbl[blk] : p.block_table[(int64_t)b * p.max_blocks + blk];
             ri = (phys >= 0 && phys < p.num_blocks) ? (phys * p.Hkv + g) * p.bs + off : -1;
         }
         rowidx[t] = ri;
@@ -168,14 +179,7 @@ __global__ __launch_bounds__(kMfmaThreads) void partition_mfma_kernel(PartitionP
         out_scale = p.v_scale[g];
     }
     __syncthreads();
-
-    uint4 qreg[2][KS];
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            qreg[rt][ks] = *reinterpret_cast<const uint4*>(qs + (rt * 16 + l16) * L::kQStride + ks * 32 + q4 * 8);
-    __syncthreads();   // Q staging area becomes V^T
+    const uint16_t* qop = qs + l16 * L::kQStride + q4 * 8;   // this lane's Q^T operand row
 
     const unsigned char* kbase = reinterpret_cast<const unsigned char*>(p.k);
     const unsigned char* vbase = reinterpret_cast<const unsigned char*>(p.v);
@@ -234,7 +238,8 @@ __global__ __launch_bounds__(kMfmaThreads) void partition_mfma_kernel(PartitionP
         for (int rt = 0; rt < 2; ++rt) {
             f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) acc = mfma_bf16(kreg[ks], qreg[rt][ks], acc);
+            for (int ks = 0; ks < KS; ++ks)
+                acc = mfma_bf16(kreg[ks], *reinterpret_cast<const uint4*>(qop + rt * 16 * L::kQStride + ks * 32), acc);
             // lane holds S^T[key t*64 + wave*16 + q4*4 + e][row rt*16 + l16]
             float4 sv;
             float* svp = reinterpret_cast<float*>(&sv);

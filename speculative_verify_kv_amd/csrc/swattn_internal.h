@@ -32,6 +32,7 @@ struct PartitionParams {
     float* ws_o;          // [B*Hkv][S][R][D] normalised partial outputs (S > 1)
     float* ws_lse;        // [B*Hkv][S][R] log2-sum-exp of each partial (S > 1)
     int32_t B, H, Hkv, G, D, bs, max_blocks, num_blocks;
+    int32_t bs_log2;      // log2(bs) when bs is a power of two, else -1
     int32_t n_q, window, R, max_ctx;
     int32_t S, rows_per_chunk, row_chunks;
     int32_t q_dtype, kv_dtype, out_dtype;
