@@ -52,7 +52,9 @@ typedef enum {
 typedef enum {
     SWATTN_OK = 0,
     SWATTN_ERR_NULL = -1,         /* a required pointer is NULL */
-    SWATTN_ERR_SHAPE = -2,        /* batch/heads/head_dim/block sizes invalid */
+    SWATTN_ERR_SHAPE = -2,        /* batch/heads/head_dim/block sizes invalid, or the launch would need
+                                     more than INT32_MAX workgroups (65535 splits or row chunks for the
+                                     matrix-core variant) */
     SWATTN_ERR_NQ = -3,           /* n_q outside [1, SWATTN_MAX_NQ] */
     SWATTN_ERR_WINDOW = -4,       /* window < 1 */
     SWATTN_ERR_DTYPE = -5,        /* unsupported dtype combination, or e4m3 without scales */
@@ -127,7 +129,8 @@ swattn_status_t swattn_workspace_bytes(const swattn_desc_t* desc, int32_t n_q, i
  *   scale       finite softmax scale (usually 1/sqrt(D))
  *   out         [B][n_q][H][D] out_dtype, device; fully overwritten; must not alias q
  *   workspace   device scratch of >= plan.workspace_bytes (may be NULL when that is 0);
- *               contents are undefined afterwards
+ *               contents are undefined afterwards; calls that overlap in time need
+ *               separate workspaces
  *   stream      hipStream_t (NULL = default stream)
  *
  * All data pointers must be 16-byte aligned.  Host-checkable errors are returned

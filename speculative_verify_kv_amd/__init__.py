@@ -62,6 +62,7 @@ class swattn_plan_t(ctypes.Structure):
 
 
 _lib = None
+ABI_VERSION = 1          # SWATTN_ABI_VERSION these ctypes mirrors follow
 
 
 def lib():
@@ -72,6 +73,10 @@ def lib():
             raise ImportError(f"{LIB_PATH} is missing: build it with "
                               "`python -m speculative_verify_kv_amd._build`")
         L = ctypes.CDLL(LIB_PATH)
+        L.swattn_abi_version.restype = ctypes.c_int32
+        if L.swattn_abi_version() != ABI_VERSION:
+            raise ImportError(f"{LIB_PATH} has ABI {L.swattn_abi_version()}, the binding expects "
+                              f"{ABI_VERSION}: rebuild it with `python -m speculative_verify_kv_amd._build`")
         P = ctypes.POINTER
         L.swattn_plan.argtypes = [P(swattn_desc_t), ctypes.c_int32, ctypes.c_int32, P(swattn_plan_t)]
         L.swattn_plan.restype = ctypes.c_int

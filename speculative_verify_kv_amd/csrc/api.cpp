@@ -96,7 +96,7 @@ extern "C" swattn_status_t swattn_verify(const swattn_desc_t* d, const void* q, 
     int err = plan.variant == SWATTN_VARIANT_MFMA ? launch_partition_mfma(p, plan.grid, stream)
                                                   : launch_partition_valu(p, plan.grid, stream);
     if (err != 0) return SWATTN_ERR_HIP;
-    if (plan.num_splits > 1) {
+    if (plan.merge_grid > 0) {
         MergeParams m;
         m.ws_o = ws_o;
         m.ws_lse = ws_lse;

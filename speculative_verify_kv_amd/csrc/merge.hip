@@ -10,7 +10,8 @@
 // union of the splits' keys exactly.
 //
 // D/4 lanes per row, each owning 4 consecutive dims (16-byte loads of every
-// partial), 1024/D rows per 256-thread workgroup.
+// partial), 1024/D rows per 256-thread workgroup.  A split with no key for the
+// row (lse = -inf) gets weight 2^-inf = 0, and so does every padding slot.
 
 #include <hip/hip_runtime.h>
 
@@ -31,19 +32,59 @@ __global__ __launch_bounds__(kBlockThreads) void merge_kernel(MergeParams p) {
     const int64_t unit = row / p.R;                 // b * Hkv + g
     const int r = (int)(row - unit * p.R);
 
+    // Splits are taken eight at a time with every load of a chunk issued before any
+    // is used; up to eight splits cost one memory round trip in all.
+    constexpr int C = 8;
     const float* lse = p.ws_lse + unit * p.S * p.R + r;
-    float M = -INFINITY;
-    for (int s = 0; s < p.S; ++s) M = fmaxf(M, lse[(int64_t)s * p.R]);
-    const float Mu = M == -INFINITY ? 0.0f : M;
-
+    const float* o = p.ws_o + (unit * p.S * p.R + r) * D + dq;
     f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
     float wsum = 0.0f;
-    const float* o = p.ws_o + (unit * p.S * p.R + r) * D + dq;
-    for (int s = 0; s < p.S; ++s) {
-        const float w = exp2f(lse[(int64_t)s * p.R] - Mu);
-        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(o + (int64_t)s * p.R * D);
-        acc += w * v;
-        wsum += w;
+    if (p.S <= C) {
+        float l[C];
+        f32x4_t v[C];
+#pragma unroll
+        for (int k = 0; k < C; ++k) {
+            const bool in = k < p.S;
+            l[k] = in ? lse[(int64_t)k * p.R] : -INFINITY;
+            v[k] = in ? *reinterpret_cast<const f32x4_t*>(o + (int64_t)k * p.R * D) : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+        float M = l[0];
+#pragma unroll
+        for (int k = 1; k < C; ++k) M = fmaxf(M, l[k]);
+        const float Mu = M == -INFINITY ? 0.0f : M;
+#pragma unroll
+        for (int k = 0; k < C; ++k) {
+            const float w = exp2f(l[k] - Mu);
+            acc += w * v[k];
+            wsum += w;
+        }
+    } else {
+        float M = -INFINITY;
+        for (int s0 = 0; s0 < p.S; s0 += C) {
+            float l[C];
+#pragma unroll
+            for (int k = 0; k < C; ++k) l[k] = s0 + k < p.S ? lse[(int64_t)(s0 + k) * p.R] : -INFINITY;
+#pragma unroll
+            for (int k = 0; k < C; ++k) M = fmaxf(M, l[k]);
+        }
+        const float Mu = M == -INFINITY ? 0.0f : M;
+        for (int s0 = 0; s0 < p.S; s0 += C) {
+            float l[C];
+            f32x4_t v[C];
+#pragma unroll
+            for (int k = 0; k < C; ++k) {
+                const bool in = s0 + k < p.S;
+                l[k] = in ? lse[(int64_t)(s0 + k) * p.R] : -INFINITY;
+                v[k] = in ? *reinterpret_cast<const f32x4_t*>(o + (int64_t)(s0 + k) * p.R * D)
+                          : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            }
+#pragma unroll
+            for (int k = 0; k < C; ++k) {
+                const float w = exp2f(l[k] - Mu);
+                acc += w * v[k];
+                wsum += w;
+            }
+        }
     }
     const f32x4_t res = acc * (1.0f / wsum);
 

@@ -93,12 +93,15 @@ swattn_status_t make_plan(const swattn_desc_t* d, int32_t n_q, int32_t window, s
     const int64_t row_chunks = (R + rows_per_chunk - 1) / rows_per_chunk;
     const int64_t grid = (int64_t)d->batch * d->num_kv_heads * row_chunks * S;
     if (grid > INT32_MAX) return SWATTN_ERR_SHAPE;
+    // the matrix-core kernel launches a (B * Hkv, row chunks, splits) grid
+    if (variant == SWATTN_VARIANT_MFMA && (row_chunks > 65535 || S > 65535)) return SWATTN_ERR_SHAPE;
 
     const int64_t rows_total = (int64_t)d->batch * d->num_kv_heads * R;
     const int64_t merge_rows_per_wg = (kBlockThreads * 4) / D;   // D/4 threads per row
     int64_t merge_grid = 0;
     size_t ws = 0;
     if (S > 1) {
+        // layout: [partial outputs][partial log2-sum-exps]
         merge_grid = (rows_total + merge_rows_per_wg - 1) / merge_rows_per_wg;
         if (merge_grid > INT32_MAX) return SWATTN_ERR_SHAPE;
         const int64_t o_bytes = ((rows_total * S * D * 4) + 255) / 256 * 256;

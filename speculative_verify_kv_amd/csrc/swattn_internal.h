@@ -11,9 +11,7 @@ namespace swattn {
 // Launch geometry shared by the planner and the kernels.
 constexpr int kWaveSize = 64;
 constexpr int kBlockThreads = 256;           // 4 waves: VALU partition and merge kernels
-constexpr int kMfmaThreads = 256;            // 4 waves: matrix-core partition kernel
 constexpr int kMfmaRows = 32;                // query rows per matrix-core workgroup (two 16-row tiles)
-constexpr int kMfmaTileKeys = 64;            // keys per online-softmax step (16 per wave)
 constexpr int kMfmaMaxKeys = 512;            // keys per matrix-core workgroup (cache-row table in LDS)
 constexpr int kValuRowsPerChunk = 8;         // query rows per VALU workgroup
 constexpr int kValuMaxKeys = 256;            // keys per VALU workgroup (score buffer size)

@@ -28,7 +28,7 @@ def test_library_exports_every_header_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert sw.swattn_abi_version() == 1
+    assert sw.swattn_abi_version() == sw.ABI_VERSION == 1
     for code in sw.STATUS:
         s = sw.swattn_status_str(code)
         assert s and s != "unknown status"
@@ -96,11 +96,15 @@ def test_plan_variants_and_workspace():
     assert p.variant == sw.SWATTN_VARIANT_MFMA and p.rows_per_chunk == 32 and p.row_chunks == 1
     assert p.grid == 24 * 2 * p.num_splits
     R, D, units = 32, 256, 24 * 2
-    if p.num_splits > 1:
-        o_bytes = -(-(units * R * p.num_splits * D * 4) // 256) * 256
-        assert p.workspace_bytes == o_bytes + units * R * p.num_splits * 4
-        assert p.merge_grid == -(-(units * R) // (1024 // D))
-    assert sw.swattn_workspace_bytes(desc(), 8, 188) == p.workspace_bytes
+    # split plans: [partial outputs][partial log2-sum-exps] and a merge launch
+    for S in (2, 5):
+        for variant in (sw.SWATTN_VARIANT_MFMA, sw.SWATTN_VARIANT_VALU):
+            p = sw.swattn_plan(desc(num_splits=S, variant=variant), 8, 188)
+            o_bytes = -(-(units * R * S * D * 4) // 256) * 256
+            assert p.num_splits == S and p.variant == variant
+            assert p.workspace_bytes == o_bytes + units * R * S * 4
+            assert p.merge_grid == -(-(units * R) // (1024 // D))
+    assert sw.swattn_workspace_bytes(desc(), 8, 188) == sw.swattn_plan(desc(), 8, 188).workspace_bytes
     # decode: 4 rows -> vector ALU
     p = sw.swattn_plan(desc(), 1, 188)
     assert p.variant == sw.SWATTN_VARIANT_VALU

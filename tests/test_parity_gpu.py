@@ -221,6 +221,27 @@ def test_check_inputs_reports_block_errors():
 
 
 # ---------------------------------------------------------------------------
+# one workspace serves plans with different split counts, results reproducible
+# ---------------------------------------------------------------------------
+def test_workspace_reuse_across_split_counts():
+    w, ref = gu.named("verify")
+    t = gu.upload(w)
+    big = sw.swattn_plan(sw.make_desc(t["q"], t["k"], t["bt"], 4096, num_splits=5), w.n_q, w.window)
+    ws = torch.full((big.workspace_bytes,), 0x7F, dtype=torch.uint8, device=gu.DEV)   # stale bytes
+    first = {}
+    for S in (2, 5, 3, 5, 2):
+        out, plan = sw.verify(t["q"], t["k"], t["v"], t["bt"], t["ctx"], w.n_q, w.window, w.scale, 4096,
+                              out_dtype=sw.SWATTN_F32, num_splits=S, workspace=ws)
+        torch.cuda.synchronize()
+        assert plan.num_splits == S
+        got = out.cpu().numpy().astype(np.float64)
+        gu.check(got, ref, w.kv_dtype, True, label=f"reuse S={S}")
+        if S in first:
+            assert np.array_equal(first[S], got), f"S={S} not reproducible"
+        first[S] = got
+
+
+# ---------------------------------------------------------------------------
 # HIP graph capture and replay
 # ---------------------------------------------------------------------------
 def test_graph_capture_replay():
