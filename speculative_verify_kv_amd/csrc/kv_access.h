@@ -33,16 +33,17 @@ __device__ __forceinline__ void e4m3x2_to_f32(uint32_t word, bool hi, float& a, 
 }
 
 // 8 E4M3 codes (little-endian in a uint2) -> 8 bfloat16 values, exactly: an E4M3
-// value has at most 4 significant bits, so keeping the upper half of its float is exact.
+// value has at most 4 significant bits and its exponent range fits bfloat16's.
+// gfx950's packed conversion with scale 1.0 (v_cvt_scalef32_pk_bf16_fp8) turns two
+// codes into two bfloat16s in one instruction; checked exhaustively against the
+// format definition for every code in every byte position.
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
 __device__ __forceinline__ uint4 e4m3x8_to_bf16x8(uint2 w) {
-    uint32_t o[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        float a, b;
-        e4m3x2_to_f32(k < 2 ? w.x : w.y, (k & 1) != 0, a, b);
-        o[k] = (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xFFFF0000u);
-    }
-    return make_uint4(o[0], o[1], o[2], o[3]);
+    const auto c = [](uint32_t word, bool hi) {
+        return __builtin_bit_cast(uint32_t, hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, true)
+                                               : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, false));
+    };
+    return make_uint4(c(w.x, false), c(w.x, true), c(w.y, false), c(w.y, true));
 }
 
 __device__ __forceinline__ uint4 ld_global_16(const void* p) {
