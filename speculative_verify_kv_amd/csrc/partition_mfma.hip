@@ -60,17 +60,23 @@ struct Geo {
     static constexpr int kNiK = kT / kRpi;                  // load instructions per K (or V) tile
     static constexpr int kTileB = kT * kRowB;               // bytes of one K (or V) tile
     static_assert(kCpr >= 4 && kCpr <= 64 && kNiK * 1024 == kTileB, "tile geometry");
-    // Workgroups per CU that the LDS allows (two stages of K and V tiles plus < 14 KiB
-    // of tables each, 160 KiB per CU).  Where only one fits, the workgroup splits the
-    // output columns across two wave sets (8 waves) so that every SIMD still holds two
-    // waves; otherwise it has 4 waves.  Either way a SIMD runs two waves, so each may
-    // hold 256 registers.
-    static constexpr int kBlocks = 2 * (4 * kTileB + 14 * 1024) <= 160 * 1024 ? 2 : 1;
+    // Stages of the K/V ring: four where two workgroups per CU still fit with them (up
+    // to three tiles in flight absorb the tail latency of a loaded memory system),
+    // else two.
+    static constexpr int kNS = 2 * (8 * kTileB + 14 * 1024) <= 160 * 1024 ? 4 : 2;
+    // Workgroups per CU that the LDS allows (the ring plus < 14 KiB of tables each,
+    // 160 KiB per CU).  Where only one fits, the workgroup splits the output columns
+    // across two wave sets (8 waves) so that every SIMD still holds two waves;
+    // otherwise it has 4 waves.  Either way a SIMD runs two waves, so each may hold
+    // 256 registers.
+    static constexpr int kBlocks = 2 * (2 * kNS * kTileB + 14 * 1024) <= 160 * 1024 ? 2 : 1;
     static constexpr int kND = kBlocks == 2 ? 1 : 2;        // column sets
     static constexpr int kNW = 4 * kND;                     // waves: 2 row blocks x 2 key halves x kND
     static constexpr int kNT = kNW * 64;
     static constexpr int kShare = 2 * kNiK / kNW;           // load instructions per wave per tile
     static_assert(kShare * kNW == 2 * kNiK && kShare <= 16, "loads split evenly over the waves");
+    static_assert(kNS == 2 || kNS == 4, "ring of 2 or 4 stages");
+    static_assert(kNS * kShare < 64, "a wave's loads in flight must fit the vmcnt counter");
     // K rows: chunk c of row k is stored at c ^ swz_k(k); 16 consecutive rows (the
     // 16 lanes of an A-operand read) land on distinct bank groups.
     static __device__ __forceinline__ int swz_k(int k) { return k & (kCpr >= 16 ? 15 : kCpr - 1); }
@@ -116,6 +122,11 @@ __device__ __forceinline__ float xgroup_sum(float x) {
     return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
 
+// 2^x by the hardware instruction alone.  Its arguments here are at most 8 (scores
+// minus a running max, or a max difference); results below the normal range
+// flush to zero, which no sum of these weights can register.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // kh ? a : b for two accumulator tiles.  The values pass through an empty asm
 // first: otherwise the compiler turns the select of two array elements into a
 // load from a selected address, and that runtime index moves the whole
@@ -157,9 +168,14 @@ __global__ __launch_bounds__((Geo<D, FP8>::kNT), (Geo<D, FP8>::kBlocks)) void pa
     constexpr int DH = D / G::kND;               // output columns of one wave set
     constexpr int DB = DH / 16;                  // 16-column output tiles per wave
     constexpr int SH = G::kShare;                // this wave's loads per tile
+    // P enters the PV product as one bfloat16 term for E4M3 caches (its rounding,
+    // below 2^-9 relative, is far inside what 8-bit values carry) and as two terms
+    // (hi + lo, about 16 bits) for bfloat16 caches, whose outputs are held to 2e-3.
+    constexpr bool kSingleP = FP8;
 
-    __shared__ __attribute__((aligned(16))) unsigned char kst[2][G::kTileB];
-    __shared__ __attribute__((aligned(16))) unsigned char vst[2][G::kTileB];
+    constexpr int NS = G::kNS;
+    __shared__ __attribute__((aligned(16))) unsigned char kst[NS][G::kTileB];
+    __shared__ __attribute__((aligned(16))) unsigned char vst[NS][G::kTileB];
     // source of every key's K and V row (a cache row, the zero row or the NaN row)
     __shared__ __attribute__((aligned(16))) const unsigned char* kptr[kMfmaMaxKeys];
     __shared__ __attribute__((aligned(16))) const unsigned char* vptr[kMfmaMaxKeys];
@@ -270,7 +286,7 @@ __global__ __launch_bounds__((Geo<D, FP8>::kNT), (Geo<D, FP8>::kBlocks)) void pa
             if (j < j0 || j >= j1) continue;
             const int ins = wave * SH + j;       // compile-time j, wave-uniform ins
             const bool is_v = ins >= G::kNiK;
-            unsigned char* dst = (is_v ? vst[t & 1] : kst[t & 1]) + (is_v ? ins - G::kNiK : ins) * 1024;
+            unsigned char* dst = (is_v ? vst[t % NS] : kst[t % NS]) + (is_v ? ins - G::kNiK : ins) * 1024;
             dma16(src[j], dst);
         }
     };
@@ -288,10 +304,10 @@ __global__ __launch_bounds__((Geo<D, FP8>::kNT), (Geo<D, FP8>::kBlocks)) void pa
     // of qreg would count them as older: the Q rows (issued with ctx_len, so landed
     // by now) are waited for here instead, before any of them is issued.
     wait_vmcnt<0>();
-    // Tiles 0 and 1 go out together: a cold round trip to memory costs about as much
-    // as computing a tile, so the first two tiles share one.
-    if (ntiles > 0) issue_range(0, 0, SH);
-    if (ntiles > 1) issue_range(1, 0, SH);
+    // The first NS tiles go out together, one per stage.
+#pragma unroll
+    for (int t = 0; t < NS; ++t)
+        if (t < ntiles) issue_range(t, 0, SH);
 
     float m_run = -INFINITY, l_run = 0.0f;   // row l16 of block rb, keys of half kh
     f32x4_t o[DB];                           // lane holds O^T[dcol0 + db*16 + 4*q4 + e][row l16]
@@ -306,58 +322,100 @@ __global__ __launch_bounds__((Geo<D, FP8>::kNT), (Geo<D, FP8>::kBlocks)) void pa
         // in two halves: at the top of tile t and after its softmax, by when the first
         // half has landed.
         constexpr int SH0 = SH > 8 ? SH / 2 : SH;
-        // this wave's loads of tile t have landed once only younger ones are pending:
-        // at t = 0 those of tile 1 (issued with tile 0), later none
-        if (t == 0 && ntiles > 1)
-            wait_vmcnt<SH>();
-        else
-            wait_vmcnt<0>();
-        __syncthreads();   // B_t: tile t is in stage t & 1 for every wave; tile t-1's stage is free
-        const bool prefetch = t >= 1 && t + 1 < ntiles;   // tile t+1 goes into tile t-1's stage
-        if (prefetch) issue_range(t + 1, 0, SH0);
-        const unsigned char* kc = kst[t & 1];
-        const unsigned char* vc = vst[t & 1];
+        // This wave's loads of tile t have landed once only those of younger tiles are
+        // pending: tiles t+1 .. t+ahead, issued before this point.
+        const int ahead = min(t == 0 ? NS - 1 : NS - 2, ntiles - 1 - t);
+        switch (ahead) {
+            case 0: wait_vmcnt<0>(); break;
+            case 1: wait_vmcnt<SH>(); break;
+            case 2: wait_vmcnt<2 * SH>(); break;
+            default: wait_vmcnt<3 * SH>(); break;
+        }
+        __syncthreads();   // B_t: tile t is in its stage for every wave; tile t-1's stage is free
+        const int tn = t + NS - 1;                         // goes into tile t-1's stage
+        const bool prefetch = t >= 1 && tn < ntiles;
+        if (prefetch) issue_range(tn, 0, SH0);
+        const unsigned char* kc = kst[t % NS];
+        const unsigned char* vc = vst[t % NS];
+        // a key half wholly past the split's end (the tail of the last tile) adds nothing
+        const int key_lo = t * kT + kbase_t;                // this wave's first key of the tile
+        const bool busy = key_lo < nk;
+        // all 32 keys inside every row's window and the split: no mask needed
+        const bool inside = key_lo + 31 < nk && k0 + key_lo >= row_lo && k0 + key_lo + 31 <= row_hi;
+        const bool unmasked = __builtin_amdgcn_ballot_w64(!inside) == 0;
 
         // ---- scores: lane holds S[row l16][key kbase_t + kb*16 + 4*q4 + e] -------------
         float sv[2][4];
+        uint4 ph, pl;
+        if (busy) {
+        // Every K operand of the tile is read first; the two key blocks then run as
+        // independent accumulation chains, interleaved.
+        uint4 ka[2][KS];                         // E4M3: 8 bytes in .x/.y, converted at use
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             const int krow = kbase_t + kb * 16 + l16;
             const unsigned char* kr = kc + krow * G::kRowB;
-            f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                uint4 a;
                 if constexpr (FP8) {
                     const int c = ks * 2 + (q4 >> 1);
                     const uint2 w =
                         *reinterpret_cast<const uint2*>(kr + ((c ^ G::swz_k(krow)) << 4) + (q4 & 1) * 8);
-                    a = e4m3x8_to_bf16x8(w);
+                    ka[kb][ks] = make_uint4(w.x, w.y, 0u, 0u);
                 } else {
                     const int c = ks * 4 + q4;
-                    a = *reinterpret_cast<const uint4*>(kr + ((c ^ G::swz_k(krow)) << 4));
+                    ka[kb][ks] = *reinterpret_cast<const uint4*>(kr + ((c ^ G::swz_k(krow)) << 4));
                 }
-                acc = mfma_bf16(a, qreg[ks], acc);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of the matrix ops
+        f32x4_t sacc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                uint4 a = ka[kb][ks];
+                if constexpr (FP8) a = e4m3x8_to_bf16x8(make_uint2(a.x, a.y));
+                sacc[kb] = mfma_bf16(a, qreg[ks], sacc[kb]);
             }
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int tt = t * kT + kbase_t + kb * 16 + q4 * 4 + e;
-                const int j = k0 + tt;
-                const bool ok = tt < nk && j >= row_lo && j <= row_hi;
-                sv[kb][e] = ok ? acc[e] * scale_log2 : -INFINITY;
+        for (int kb = 0; kb < 2; ++kb) {
+            const f32x4_t acc = sacc[kb];
+            if (unmasked) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sv[kb][e] = acc[e] * scale_log2;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int tt = key_lo + kb * 16 + q4 * 4 + e;
+                    const int j = k0 + tt;
+                    const bool ok = tt < nk && j >= row_lo && j <= row_hi;
+                    sv[kb][e] = ok ? acc[e] * scale_log2 : -INFINITY;
+                }
             }
         }
 
         // ---- online softmax in registers --------------------------------------------
+        // The running max m_run only moves when a row's tile max exceeds it by more than
+        // 2^8: P = 2^(S - m_run) stays below 256, and the rescale of O^T (a multiply per
+        // accumulator) is skipped on every tile where no row of the wave moves.  The
+        // result is the same softmax: O^T and the sum carry the same reference max.
         float mt = sv[0][0];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int e = 0; e < 4; ++e) mt = fmaxf(mt, sv[kb][e]);
         mt = xgroup_max(mt);
-        const float m_new = fmaxf(m_run, mt);
-        const float mu = m_new == -INFINITY ? 0.0f : m_new;
-        const float alpha = exp2f(m_run - mu);
+        const bool grow = mt > m_run + 8.0f;                // never for a row with no key yet
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+            const float m_new = grow ? mt : m_run;
+            const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.0f : m_new));
+#pragma unroll
+            for (int db = 0; db < DB; ++db) o[db] = o[db] * alpha;
+            l_run *= alpha;
+            m_run = m_new;
+        }
+        const float mu = m_run == -INFINITY ? 0.0f : m_run;
         float psum = 0.0f;
         // B operand of the PV step: k-slot hh*4 + e <-> key kbase_t + hh*16 + 4*q4 + e
         uint32_t wh[4], wl[4];
@@ -365,22 +423,27 @@ __global__ __launch_bounds__((Geo<D, FP8>::kNT), (Geo<D, FP8>::kBlocks)) void pa
         for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
             for (int e2 = 0; e2 < 2; ++e2) {
-                const float p0 = exp2f(sv[hh][2 * e2] - mu);
-                const float p1 = exp2f(sv[hh][2 * e2 + 1] - mu);
+                const float p0 = fast_exp2(sv[hh][2 * e2] - mu);
+                const float p1 = fast_exp2(sv[hh][2 * e2 + 1] - mu);
                 const uint32_t h0 = f32_to_bf16_bits(p0), h1 = f32_to_bf16_bits(p1);
-                const uint32_t r0 = f32_to_bf16_bits(p0 - bf16_bits_to_f32(h0));
-                const uint32_t r1 = f32_to_bf16_bits(p1 - bf16_bits_to_f32(h1));
                 psum += p0 + p1;
                 wh[hh * 2 + e2] = h0 | (h1 << 16);
-                wl[hh * 2 + e2] = r0 | (r1 << 16);
+                if constexpr (!kSingleP) {
+                    const uint32_t r0 = f32_to_bf16_bits(p0 - bf16_bits_to_f32(h0));
+                    const uint32_t r1 = f32_to_bf16_bits(p1 - bf16_bits_to_f32(h1));
+                    wl[hh * 2 + e2] = r0 | (r1 << 16);
+                } else {
+                    wl[hh * 2 + e2] = 0u;
+                }
             }
         }
-        const uint4 ph = make_uint4(wh[0], wh[1], wh[2], wh[3]);
-        const uint4 pl = make_uint4(wl[0], wl[1], wl[2], wl[3]);
-        l_run = l_run * alpha + xgroup_sum(psum);
-        m_run = m_new;
+        ph = make_uint4(wh[0], wh[1], wh[2], wh[3]);
+        pl = make_uint4(wl[0], wl[1], wl[2], wl[3]);
+        l_run += xgroup_sum(psum);
+        }   // busy
 
-        if (SH0 < SH && prefetch) issue_range(t + 1, SH0, SH);
+        if (SH0 < SH && prefetch) issue_range(tn, SH0, SH);
+        if (!busy) continue;
 
         // ---- O^T = alpha O^T + V^T P^T ----------------------------------------------
         // Software-pipelined by hand: the V^T reads of step db+1 go out before the
@@ -414,17 +477,19 @@ __global__ __launch_bounds__((Geo<D, FP8>::kNT), (Geo<D, FP8>::kBlocks)) void pa
             }
             return a;
         };
-        uint4 a_cur = load_vt(0);
+        // every V^T operand first, then one matrix op per accumulator for the hi term
+        // and one more for the lo term, so that consecutive ops are independent
+        uint4 va[DB];
+#pragma unroll
+        for (int db = 0; db < DB; ++db) va[db] = load_vt(db);
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-            const uint4 a_next = db + 1 < DB ? load_vt(db + 1) : a_cur;
-            uint4 a = a_cur;
-            if constexpr (FP8) a = e4m3x8_to_bf16x8(make_uint2(a_cur.x, a_cur.y));
-            f32x4_t acc = o[db] * alpha;
-            acc = mfma_bf16(a, ph, acc);
-            o[db] = mfma_bf16(a, pl, acc);
-            __builtin_amdgcn_sched_barrier(0);
-            a_cur = a_next;
+            if constexpr (FP8) va[db] = e4m3x8_to_bf16x8(make_uint2(va[db].x, va[db].y));
+            o[db] = mfma_bf16(va[db], ph, o[db]);
+        }
+        if constexpr (!kSingleP) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db) o[db] = mfma_bf16(va[db], pl, o[db]);
         }
     }
 

@@ -158,6 +158,28 @@ def test_one_hot_values_expose_mask(variant):
         np.testing.assert_allclose(g, wref, rtol=0, atol=2e-3)
 
 
+# ---------------------------------------------------------------------------
+# scores that grow along the window move the running max on late tiles too
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("variant", [sw.SWATTN_VARIANT_MFMA, sw.SWATTN_VARIANT_VALU])
+def test_rising_scores_rescale_on_late_tiles(variant):
+    w = synth.make_workload("rise", B=2, H=8, Hkv=2, D=256, n_q=8, window=188, ctx=[4096, 700],
+                            bs=16, seed=12, recent=195)
+    lo, hi = oracle.window_bounds(w.ctx_len, w.n_q, w.window)
+    for b in range(w.B):
+        u_lo = int(lo[b, 0])
+        for j in range(u_lo, int(hi[b, -1]) + 1):
+            # K rows grow by 2^(1/48) per position: the tile maxima of the scores rise
+            # by far more than 2^8 from one 64-key tile to the next
+            blk, off = w.block_table[b, j // w.bs], j % w.bs
+            row = (w.k_cache[blk, :, off, :].astype(np.uint32) << 16).view(np.float32)
+            w.k_cache[blk, :, off, :] = synth.to_bf16_bits(row * np.float32(2.0 ** ((j - u_lo) / 48.0)))
+    ref = gu.reference(w)
+    for S, out_f32 in ((1, True), (1, False), (2, True)):
+        got, plan = gu.run(w, out_f32=out_f32, num_splits=S, variant=variant)
+        gu.check(got, ref, w.kv_dtype, out_f32, label=f"rise S={S} f32={out_f32}")
+
+
 def test_window_one_returns_own_value_row_exactly():
     w = synth.make_workload("w1", B=2, H=8, Hkv=2, D=128, n_q=8, window=1, ctx=[40, 17], bs=16, seed=8)
     for variant, out_f32 in ((sw.SWATTN_VARIANT_MFMA, False), (sw.SWATTN_VARIANT_MFMA, True),
