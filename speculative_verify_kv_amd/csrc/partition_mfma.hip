@@ -317,11 +317,6 @@ __global__ __launch_bounds__((Geo<D, FP8>::kNT), (Geo<D, FP8>::kBlocks)) void pa
     const int kbase_t = kh * 32;             // this wave's keys within a tile
 
     for (int t = 0; t < ntiles; ++t) {
-        // A wave keeps about eight vector-memory instructions in flight; a ninth waits
-        // for the oldest.  So a share of more than eight of tile t+1's loads goes out
-        // in two halves: at the top of tile t and after its softmax, by when the first
-        // half has landed.
-        constexpr int SH0 = SH > 8 ? SH / 2 : SH;
         // This wave's loads of tile t have landed once only those of younger tiles are
         // pending: tiles t+1 .. t+ahead, issued before this point.
         const int ahead = min(t == 0 ? NS - 1 : NS - 2, ntiles - 1 - t);
@@ -334,20 +329,35 @@ __global__ __launch_bounds__((Geo<D, FP8>::kNT), (Geo<D, FP8>::kBlocks)) void pa
         __syncthreads();   // B_t: tile t is in its stage for every wave; tile t-1's stage is free
         const int tn = t + NS - 1;                         // goes into tile t-1's stage
         const bool prefetch = t >= 1 && tn < ntiles;
-        if (prefetch) issue_range(tn, 0, SH0);
+        // This wave's loads of tile tn go out between the matrix ops of the scores
+        // below: a load instruction can stall its wave at issue while the memory
+        // pipeline is busy, and the matrix ops already issued keep running meanwhile.
+        const unsigned char* src[SH];
+        if (prefetch) rows_of(tn, src);
+        auto load_one = [=](int j, const unsigned char* from) __attribute__((always_inline)) {
+            const int ins = wave * SH + j;       // compile-time j, wave-uniform ins
+            const bool is_v = ins >= G::kNiK;
+            dma16(from, (is_v ? vst[tn % NS] : kst[tn % NS]) + (is_v ? ins - G::kNiK : ins) * 1024);
+        };
+        constexpr int kPerStep = (SH + KS - 1) / KS;        // loads after each k-step's matrix ops
         const unsigned char* kc = kst[t % NS];
         const unsigned char* vc = vst[t % NS];
         // a key half wholly past the split's end (the tail of the last tile) adds nothing
         const int key_lo = t * kT + kbase_t;                // this wave's first key of the tile
-        const bool busy = key_lo < nk;
+        if (key_lo >= nk) {
+            if (prefetch) {
+#pragma unroll
+                for (int j = 0; j < SH; ++j) load_one(j, src[j]);
+            }
+            continue;
+        }
         // all 32 keys inside every row's window and the split: no mask needed
         const bool inside = key_lo + 31 < nk && k0 + key_lo >= row_lo && k0 + key_lo + 31 <= row_hi;
         const bool unmasked = __builtin_amdgcn_ballot_w64(!inside) == 0;
 
         // ---- scores: lane holds S[row l16][key kbase_t + kb*16 + 4*q4 + e] -------------
         float sv[2][4];
-        uint4 ph, pl;
-        if (busy) {
+        {
         // Every K operand of the tile is read first; the two key blocks then run as
         // independent accumulation chains, interleaved.
         uint4 ka[2][KS];                         // E4M3: 8 bytes in .x/.y, converted at use
@@ -371,13 +381,19 @@ __global__ __launch_bounds__((Geo<D, FP8>::kNT), (Geo<D, FP8>::kBlocks)) void pa
         __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of the matrix ops
         f32x4_t sacc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
+        for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
                 uint4 a = ka[kb][ks];
                 if constexpr (FP8) a = e4m3x8_to_bf16x8(make_uint2(a.x, a.y));
                 sacc[kb] = mfma_bf16(a, qreg[ks], sacc[kb]);
             }
+            if (prefetch) {
+#pragma unroll
+                for (int j = ks * kPerStep; j < (ks + 1) * kPerStep && j < SH; ++j) load_one(j, src[j]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             const f32x4_t acc = sacc[kb];
@@ -394,6 +410,8 @@ __global__ __launch_bounds__((Geo<D, FP8>::kNT), (Geo<D, FP8>::kBlocks)) void pa
                 }
             }
         }
+
+        }   // scores
 
         // ---- online softmax in registers --------------------------------------------
         // The running max m_run only moves when a row's tile max exceeds it by more than
@@ -437,13 +455,9 @@ __global__ __launch_bounds__((Geo<D, FP8>::kNT), (Geo<D, FP8>::kBlocks)) void pa
                 }
             }
         }
-        ph = make_uint4(wh[0], wh[1], wh[2], wh[3]);
-        pl = make_uint4(wl[0], wl[1], wl[2], wl[3]);
+        const uint4 ph = make_uint4(wh[0], wh[1], wh[2], wh[3]);
+        const uint4 pl = make_uint4(wl[0], wl[1], wl[2], wl[3]);
         l_run += xgroup_sum(psum);
-        }   // busy
-
-        if (SH0 < SH && prefetch) issue_range(tn, SH0, SH);
-        if (!busy) continue;
 
         // ---- O^T = alpha O^T + V^T P^T ----------------------------------------------
         // Software-pipelined by hand: the V^T reads of step db+1 go out before the
