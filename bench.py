@@ -46,6 +46,8 @@ DESCRIPTIONS = {
                     "ctx ~ U[188, 4096], window 188, n_q 8, block 16, seed 4",
     "wide_verify": "wide verify: 24 layers x (8 q / 2 kv heads), head_dim 256, bf16, ctx 4096, window 188, "
                    "n_q 64, 5% of Q rows x8, block 16, seed 3",
+    "prefill_512": "chunked prefill: 24 layers x (8 q / 2 kv heads), head_dim 256, bf16, the last 512-token "
+                   "chunk of a 4096-token prompt, window 188, block 16, seed 5",
 }
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_verify_24x2kv_d256_w188_nq8.txt")
 KERNEL_SOURCES = ["partition_mfma.hip", "partition_valu.hip", "merge.hip", "kv_access.h",
@@ -170,13 +172,16 @@ def main():
     ctx = torch.from_numpy(w.ctx_len).to(dev)
     max_ctx = int(w.ctx_len.max())
     desc = sw.make_desc(q, k, bt, max_ctx, k_scale=ks, v_scale=vs, num_splits=args.splits)
-    plan = sw.swattn_plan(desc, w.n_q, w.window)
+    # a chunk of more than 64 new positions is a prefill chunk: same attention, other entry point
+    prefill = w.n_q > sw.SWATTN_MAX_NQ
+    plan = (sw.swattn_prefill_plan if prefill else sw.swattn_plan)(desc, w.n_q, w.window)
+    call_lib = sw.swattn_prefill if prefill else sw.swattn_verify
     out = torch.empty(q.shape, dtype=torch.float32 if w.q_dtype == "f32" else torch.bfloat16, device=dev)
     ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def call():
-        sw.swattn_verify(desc, q, k, v, bt, ctx, w.n_q, w.window, w.scale, out, ws,
+        call_lib(desc, q, k, v, bt, ctx, w.n_q, w.window, w.scale, out, ws,
                          plan.workspace_bytes, stream.cuda_stream)
 
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
@@ -210,7 +215,7 @@ def main():
             for _ in range(args.steps):
                 flush.zero_()
                 if with_calls:
-                    sw.swattn_verify(desc, q, k, v, bt, ctx, w.n_q, w.window, w.scale, out, ws,
+                    call_lib(desc, q, k, v, bt, ctx, w.n_q, w.window, w.scale, out, ws,
                                      plan.workspace_bytes, cs)
         return g
 
@@ -268,7 +273,7 @@ def main():
         with torch.cuda.graph(g):
             cs = torch.cuda.current_stream(dev).cuda_stream
             for _ in range(100):
-                sw.swattn_verify(desc, q, k, v, bt, ctx, w.n_q, w.window, w.scale, out, ws,
+                call_lib(desc, q, k, v, bt, ctx, w.n_q, w.window, w.scale, out, ws,
                                  plan.workspace_bytes, cs)
         g.replay()
         torch.cuda.synchronize()

@@ -42,6 +42,7 @@ extern "C" {
 
 #define SWATTN_ABI_VERSION 1
 #define SWATTN_MAX_NQ 64          /* SPLITKV_VERIFY_MAX_Q of the manifest */
+#define SWATTN_MAX_PREFILL_NQ 512 /* MAX_NUM_BATCHED_TOKENS of the manifest */
 
 typedef enum {
     SWATTN_F32 = 0,               /* IEEE binary32 */
@@ -55,7 +56,7 @@ typedef enum {
     SWATTN_ERR_SHAPE = -2,        /* batch/heads/head_dim/block sizes invalid, or the launch would need
                                      more than INT32_MAX workgroups (65535 splits or row chunks for the
                                      matrix-core variant) */
-    SWATTN_ERR_NQ = -3,           /* n_q outside [1, SWATTN_MAX_NQ] */
+    SWATTN_ERR_NQ = -3,           /* n_q outside [1, SWATTN_MAX_NQ] (prefill: [1, SWATTN_MAX_PREFILL_NQ]) */
     SWATTN_ERR_WINDOW = -4,       /* window < 1 */
     SWATTN_ERR_DTYPE = -5,        /* unsupported dtype combination, or e4m3 without scales */
     SWATTN_ERR_ALIGN = -6,        /* a data pointer is not 16-byte aligned */
@@ -150,8 +151,31 @@ swattn_status_t swattn_verify(const swattn_desc_t* desc,
                               void* stream);
 
 /*
- * swattn_check_inputs — debug check of the device-resident preconditions.
- * Copies ctx_len and block_table to the host (synchronising the stream) and
+ * swattn_prefill_plan / swattn_prefill — the same attention for a chunk of up to
+ * SWATTN_MAX_PREFILL_NQ new positions per sequence (chunked prefill).
+ *
+ * Source: "The Fast Gemma Challenge: our verified-SOTA recipe, in full" (dev.to,
+ * VIDRAFT), full manifest.json — MAX_NUM_BATCHED_TOKENS=512 caps the tokens of one
+ * engine step, prefill chunks included, while SPLITKV_VERIFY_MAX_Q=64 caps the verify
+ * path; a prefill chunk therefore takes the same windowed attention with n_q above 64.
+ * Arguments, layouts, ownership, alignment, workspace and error behaviour are those of
+ * swattn_plan / swattn_verify, with n_q in [1, SWATTN_MAX_PREFILL_NQ].  Each 32-row
+ * (or 8-row) chunk of query rows scans only the union of its own rows' windows, so the
+ * work grows with n_q * window, not n_q * (window + n_q).
+ */
+swattn_status_t swattn_prefill_plan(const swattn_desc_t* desc, int32_t n_q, int32_t window,
+                                    swattn_plan_t* plan);
+
+swattn_status_t swattn_prefill(const swattn_desc_t* desc,
+                               const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* block_table, const int32_t* ctx_len,
+                               int32_t n_q, int32_t window, float scale,
+                               void* out, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/*
+ * swattn_check_inputs — debug check of the device-resident preconditions (n_q up to
+ * SWATTN_MAX_PREFILL_NQ).  Copies ctx_len and block_table to the host (synchronising the stream) and
  * returns SWATTN_ERR_CTX if some ctx_len[b] lies outside
  * [n_q, min(max_ctx_len, max_blocks_per_seq*block_size)], SWATTN_ERR_BLOCK if a block id that a
  * window reads lies outside [0, num_blocks), SWATTN_OK otherwise.  Allocates

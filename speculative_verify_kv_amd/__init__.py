@@ -3,9 +3,10 @@
 Argument marshalling only: every step of the computation runs in the HIP
 kernels of ``libswattn.so``.  The functions mirror the C ABI in
 ``include/swattn.h`` one for one (``swattn_plan``, ``swattn_workspace_bytes``,
-``swattn_verify``, ``swattn_check_inputs``, ``swattn_status_str``,
-``swattn_abi_version``); ``verify`` is a convenience that fills the descriptor
-from torch tensors and runs on torch's current HIP stream.  There is no CPU
+``swattn_verify``, ``swattn_prefill_plan``, ``swattn_prefill``,
+``swattn_check_inputs``, ``swattn_status_str``, ``swattn_abi_version``);
+``verify`` and ``prefill`` are conveniences that fill the descriptor from torch
+tensors and run on torch's current HIP stream.  There is no CPU
 fallback: if the library is missing, loading fails with an error.
 """
 import ctypes
@@ -17,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libswattn.so")
 SWATTN_F32, SWATTN_BF16, SWATTN_FP8_E4M3 = 0, 1, 2
 SWATTN_VARIANT_AUTO, SWATTN_VARIANT_VALU, SWATTN_VARIANT_MFMA = 0, 1, 2
 SWATTN_MAX_NQ = 64
+SWATTN_MAX_PREFILL_NQ = 512
 
 STATUS = {
     0: "SWATTN_OK", -1: "SWATTN_ERR_NULL", -2: "SWATTN_ERR_SHAPE", -3: "SWATTN_ERR_NQ",
@@ -26,8 +28,8 @@ STATUS = {
 }
 
 # Symbols declared in include/swattn.h.
-EXPORTED = ("swattn_plan", "swattn_workspace_bytes", "swattn_verify", "swattn_check_inputs",
-            "swattn_status_str", "swattn_abi_version")
+EXPORTED = ("swattn_plan", "swattn_workspace_bytes", "swattn_verify", "swattn_prefill_plan",
+            "swattn_prefill", "swattn_check_inputs", "swattn_status_str", "swattn_abi_version")
 
 
 class SwattnError(RuntimeError):
@@ -88,6 +90,10 @@ def lib():
                                     ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                     ctypes.c_void_p]
         L.swattn_verify.restype = ctypes.c_int
+        L.swattn_prefill_plan.argtypes = L.swattn_plan.argtypes
+        L.swattn_prefill_plan.restype = ctypes.c_int
+        L.swattn_prefill.argtypes = L.swattn_verify.argtypes
+        L.swattn_prefill.restype = ctypes.c_int
         L.swattn_check_inputs.argtypes = [P(swattn_desc_t), ctypes.c_void_p, ctypes.c_void_p,
                                           ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
         L.swattn_check_inputs.restype = ctypes.c_int
@@ -124,6 +130,14 @@ def swattn_plan(desc, n_q, window, check=True):
     return plan if check else (st, plan)
 
 
+def swattn_prefill_plan(desc, n_q, window, check=True):
+    plan = swattn_plan_t()
+    st = lib().swattn_prefill_plan(ctypes.byref(desc), int(n_q), int(window), ctypes.byref(plan))
+    if check and st != 0:
+        raise SwattnError(st, "swattn_prefill_plan")
+    return plan if check else (st, plan)
+
+
 def swattn_workspace_bytes(desc, n_q, window):
     n = ctypes.c_size_t(0)
     st = lib().swattn_workspace_bytes(ctypes.byref(desc), int(n_q), int(window), ctypes.byref(n))
@@ -140,6 +154,17 @@ def swattn_verify(desc, q, k_cache, v_cache, block_table, ctx_len, n_q, window, 
                              _ptr(stream))
     if check and st != 0:
         raise SwattnError(st, "swattn_verify")
+    return st
+
+
+def swattn_prefill(desc, q, k_cache, v_cache, block_table, ctx_len, n_q, window, scale, out,
+                   workspace=None, workspace_bytes=0, stream=None, check=True):
+    st = lib().swattn_prefill(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                              _ptr(block_table), _ptr(ctx_len), int(n_q), int(window),
+                              float(scale), _ptr(out), _ptr(workspace), int(workspace_bytes),
+                              _ptr(stream))
+    if check and st != 0:
+        raise SwattnError(st, "swattn_prefill")
     return st
 
 
@@ -182,15 +207,15 @@ def make_desc(q, k_cache, block_table, max_ctx_len, out_dtype=None, k_scale=None
 
 def verify(q, k_cache, v_cache, block_table, ctx_len, n_q, window, scale, max_ctx_len,
            out=None, out_dtype=None, k_scale=None, v_scale=None, num_splits=0,
-           variant=SWATTN_VARIANT_AUTO, workspace=None, stream=None):
-    """Run swattn_verify on torch device tensors; returns (out, plan).
+           variant=SWATTN_VARIANT_AUTO, workspace=None, stream=None, prefill=False):
+    """Run swattn_verify (or swattn_prefill) on torch device tensors; returns (out, plan).
 
     Allocates ``out`` and the workspace with torch when they are not given (a
     caller under graph capture passes both)."""
     import torch
     desc = make_desc(q, k_cache, block_table, max_ctx_len, out_dtype, k_scale, v_scale,
                      num_splits, variant)
-    plan = swattn_plan(desc, n_q, window)
+    plan = (swattn_prefill_plan if prefill else swattn_plan)(desc, n_q, window)
     if out is None:
         tdt = torch.float32 if desc.out_dtype == SWATTN_F32 else torch.bfloat16
         out = torch.empty(q.shape, dtype=tdt, device=q.device)
@@ -199,6 +224,12 @@ def verify(q, k_cache, v_cache, block_table, ctx_len, n_q, window, scale, max_ct
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
-    swattn_verify(desc, q, k_cache, v_cache, block_table, ctx_len, n_q, window, scale, out,
-                  workspace, ws_bytes, stream)
+    (swattn_prefill if prefill else swattn_verify)(desc, q, k_cache, v_cache, block_table, ctx_len, n_q,
+                                                   window, scale, out, workspace, ws_bytes, stream)
     return out, plan
+
+
+def prefill(q, k_cache, v_cache, block_table, ctx_len, n_q, window, scale, max_ctx_len, **kw):
+    """Run swattn_prefill (n_q up to SWATTN_MAX_PREFILL_NQ); arguments as ``verify``."""
+    return verify(q, k_cache, v_cache, block_table, ctx_len, n_q, window, scale, max_ctx_len,
+                  prefill=True, **kw)

@@ -10,8 +10,9 @@
 #include "swattn_internal.h"
 
 namespace swattn {
-swattn_status_t validate_desc(const swattn_desc_t* d, int32_t n_q, int32_t window);
-swattn_status_t make_plan(const swattn_desc_t* d, int32_t n_q, int32_t window, swattn_plan_t* out);
+swattn_status_t validate_desc(const swattn_desc_t* d, int32_t n_q, int32_t window, int32_t max_nq);
+swattn_status_t make_plan(const swattn_desc_t* d, int32_t n_q, int32_t window, int32_t max_nq,
+                          swattn_plan_t* out);
 
 namespace {
 
@@ -22,13 +23,16 @@ int dtype_bytes(int dt) { return dt == SWATTN_F32 ? 4 : (dt == SWATTN_BF16 ? 2 :
 }  // namespace
 }  // namespace swattn
 
-extern "C" swattn_status_t swattn_verify(const swattn_desc_t* d, const void* q, const void* k_cache,
-                                         const void* v_cache, const int32_t* block_table,
-                                         const int32_t* ctx_len, int32_t n_q, int32_t window, float scale,
-                                         void* out, void* workspace, size_t workspace_bytes, void* stream) {
-    using namespace swattn;
+namespace swattn {
+namespace {
+
+// One attention call (verify or prefill: they differ only in the n_q cap).
+swattn_status_t attend(const swattn_desc_t* d, const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_table, const int32_t* ctx_len, int32_t n_q, int32_t window,
+                       float scale, void* out, void* workspace, size_t workspace_bytes, void* stream,
+                       int32_t max_nq) {
     swattn_plan_t plan;
-    swattn_status_t st = make_plan(d, n_q, window, &plan);
+    swattn_status_t st = make_plan(d, n_q, window, max_nq, &plan);
     if (st != SWATTN_OK) return st;
     if (!q || !k_cache || !v_cache || !block_table || !ctx_len || !out) return SWATTN_ERR_NULL;
     if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
@@ -116,11 +120,30 @@ extern "C" swattn_status_t swattn_verify(const swattn_desc_t* d, const void* q, 
     return SWATTN_OK;
 }
 
+}  // namespace
+}  // namespace swattn
+
+extern "C" swattn_status_t swattn_verify(const swattn_desc_t* d, const void* q, const void* k_cache,
+                                         const void* v_cache, const int32_t* block_table,
+                                         const int32_t* ctx_len, int32_t n_q, int32_t window, float scale,
+                                         void* out, void* workspace, size_t workspace_bytes, void* stream) {
+    return swattn::attend(d, q, k_cache, v_cache, block_table, ctx_len, n_q, window, scale, out, workspace,
+                          workspace_bytes, stream, SWATTN_MAX_NQ);
+}
+
+extern "C" swattn_status_t swattn_prefill(const swattn_desc_t* d, const void* q, const void* k_cache,
+                                          const void* v_cache, const int32_t* block_table,
+                                          const int32_t* ctx_len, int32_t n_q, int32_t window, float scale,
+                                          void* out, void* workspace, size_t workspace_bytes, void* stream) {
+    return swattn::attend(d, q, k_cache, v_cache, block_table, ctx_len, n_q, window, scale, out, workspace,
+                          workspace_bytes, stream, SWATTN_MAX_PREFILL_NQ);
+}
+
 extern "C" swattn_status_t swattn_check_inputs(const swattn_desc_t* d, const int32_t* block_table,
                                                const int32_t* ctx_len, int32_t n_q, int32_t window,
                                                void* stream) {
     using namespace swattn;
-    swattn_status_t st = validate_desc(d, n_q, window);
+    swattn_status_t st = validate_desc(d, n_q, window, SWATTN_MAX_PREFILL_NQ);
     if (st != SWATTN_OK) return st;
     if (!block_table || !ctx_len) return SWATTN_ERR_NULL;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);

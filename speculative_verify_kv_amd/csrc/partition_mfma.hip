@@ -221,12 +221,17 @@ __global__ __launch_bounds__((Geo<D, FP8>::kNT), (Geo<D, FP8>::kBlocks)) void pa
     const int ctx = p.ctx_len[b];
     const bool seq_ok = ctx >= p.n_q && ctx <= p.max_blocks * p.bs && ctx <= p.max_ctx;
     const int pos0 = seq_ok ? ctx - p.n_q : 0;             // position of query 0
-    const int u_lo = max(0, pos0 - p.window + 1);          // first key of the step's union window
+    // The chunk's keys: the union of its rows' windows, queries qi_lo .. qi_hi, i.e.
+    // positions [pos0 + qi_lo - W + 1, pos0 + qi_hi]; the split takes a 1/S share.
+    const int qi_lo = rc * kMfmaRows / p.G;
+    const int qi_hi = min(p.R - 1, rc * kMfmaRows + kMfmaRows - 1) / p.G;
+    const int u_lo = max(0, pos0 + qi_lo - p.window + 1);
+    const int u_hi = pos0 + qi_hi + 1;                     // one past the last key
     int k0 = 0, nk = 0;
     if (seq_ok) {
-        const int kps = (ctx - u_lo + p.S - 1) / p.S;
+        const int kps = (u_hi - u_lo + p.S - 1) / p.S;
         k0 = u_lo + s * kps;
-        nk = max(0, min(ctx, k0 + kps) - k0);              // <= kMfmaMaxKeys by the plan
+        nk = max(0, min(u_hi, k0 + kps) - k0);             // <= kMfmaMaxKeys by the plan
     }
     const int ntiles = (nk + kT - 1) / kT;
     if (short_row) tbl[tid] = tb;

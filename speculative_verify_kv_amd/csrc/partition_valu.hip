@@ -114,13 +114,16 @@ __global__ __launch_bounds__(kBlockThreads) void partition_valu_kernel(Partition
     const int ctx = p.ctx_len[b];
     const bool seq_ok = ctx >= p.n_q && ctx <= p.max_blocks * p.bs && ctx <= p.max_ctx;
     const int pos0 = seq_ok ? ctx - p.n_q : 0;
-    const int u_lo = max(0, pos0 - p.window + 1);
+    // the chunk's keys: the union of its rows' windows (queries qi_lo .. qi_hi)
+    const int qi_lo = rc * p.rows_per_chunk / p.G;
+    const int qi_hi = min(p.R - 1, rc * p.rows_per_chunk + p.rows_per_chunk - 1) / p.G;
+    const int u_lo = max(0, pos0 + qi_lo - p.window + 1);
+    const int u_hi = pos0 + qi_hi + 1;                   // one past the last key
     int k0 = 0, nk = 0;
     if (seq_ok) {
-        const int ub = ctx - u_lo;                       // keys in the union window
-        const int kps = (ub + p.S - 1) / p.S;
+        const int kps = (u_hi - u_lo + p.S - 1) / p.S;
         k0 = u_lo + s * kps;
-        nk = max(0, min(ctx, k0 + kps) - k0);
+        nk = max(0, min(u_hi, k0 + kps) - k0);
     }
 
     float sl2 = p.scale_log2;

@@ -26,7 +26,7 @@ int64_t clamp64(int64_t v, int64_t lo, int64_t hi) { return v < lo ? lo : (v > h
 
 }  // namespace
 
-swattn_status_t validate_desc(const swattn_desc_t* d, int32_t n_q, int32_t window) {
+swattn_status_t validate_desc(const swattn_desc_t* d, int32_t n_q, int32_t window, int32_t max_nq) {
     if (!d) return SWATTN_ERR_NULL;
     if (d->batch < 1 || d->num_heads < 1 || d->num_kv_heads < 1 ||
         d->num_heads % d->num_kv_heads != 0)
@@ -39,7 +39,7 @@ swattn_status_t validate_desc(const swattn_desc_t* d, int32_t n_q, int32_t windo
     // cache rows are indexed with 32-bit integers inside the kernels
     if ((int64_t)d->num_blocks * d->num_kv_heads * d->block_size > INT32_MAX) return SWATTN_ERR_SHAPE;
     if ((int64_t)d->max_blocks_per_seq * d->block_size > INT32_MAX) return SWATTN_ERR_SHAPE;
-    if (n_q < 1 || n_q > SWATTN_MAX_NQ) return SWATTN_ERR_NQ;
+    if (n_q < 1 || n_q > max_nq) return SWATTN_ERR_NQ;
     if (window < 1) return SWATTN_ERR_WINDOW;
     if (d->max_ctx_len < n_q) return SWATTN_ERR_CTX;
     if (!dtype_in(d->q_dtype, {SWATTN_F32, SWATTN_BF16})) return SWATTN_ERR_DTYPE;
@@ -57,19 +57,26 @@ swattn_status_t validate_desc(const swattn_desc_t* d, int32_t n_q, int32_t windo
     return SWATTN_OK;
 }
 
-swattn_status_t make_plan(const swattn_desc_t* d, int32_t n_q, int32_t window, swattn_plan_t* out) {
-    swattn_status_t st = validate_desc(d, n_q, window);
+swattn_status_t make_plan(const swattn_desc_t* d, int32_t n_q, int32_t window, int32_t max_nq,
+                          swattn_plan_t* out) {
+    swattn_status_t st = validate_desc(d, n_q, window, max_nq);
     if (st != SWATTN_OK) return st;
     if (!out) return SWATTN_ERR_NULL;
 
     const int64_t G = d->num_heads / d->num_kv_heads;
     const int64_t R = (int64_t)n_q * G;                       // query rows per (problem, KV head)
     const int64_t D = d->head_dim;
-    const int64_t U = std::min<int64_t>(d->max_ctx_len, (int64_t)window + n_q - 1);  // union keys
     const bool mfma_ok = d->q_dtype == SWATTN_BF16 && d->kv_dtype != SWATTN_F32;
 
     int variant = d->variant;
     if (variant == SWATTN_VARIANT_AUTO) variant = (mfma_ok && R >= 16) ? SWATTN_VARIANT_MFMA : SWATTN_VARIANT_VALU;
+
+    // A row chunk scans the union of its own rows' windows: its queries (at most
+    // (rows_per_chunk - 1) / G + 2 of them, fewer when n_q is smaller) add one key each
+    // to the window.
+    const int64_t rpc = variant == SWATTN_VARIANT_MFMA ? kMfmaRows : kValuRowsPerChunk;
+    const int64_t qpc = std::min<int64_t>(n_q, (rpc - 1) / G + 2);
+    const int64_t U = std::min<int64_t>(d->max_ctx_len, (int64_t)window + qpc - 1);   // keys per chunk
 
     int64_t rows_per_chunk, S;
     if (variant == SWATTN_VARIANT_MFMA) {
@@ -124,7 +131,15 @@ extern "C" {
 swattn_status_t swattn_plan(const swattn_desc_t* desc, int32_t n_q, int32_t window, swattn_plan_t* plan) {
     if (!plan) return SWATTN_ERR_NULL;
     swattn_plan_t tmp;
-    swattn_status_t st = swattn::make_plan(desc, n_q, window, &tmp);
+    swattn_status_t st = swattn::make_plan(desc, n_q, window, SWATTN_MAX_NQ, &tmp);
+    if (st == SWATTN_OK) *plan = tmp;
+    return st;
+}
+
+swattn_status_t swattn_prefill_plan(const swattn_desc_t* desc, int32_t n_q, int32_t window, swattn_plan_t* plan) {
+    if (!plan) return SWATTN_ERR_NULL;
+    swattn_plan_t tmp;
+    swattn_status_t st = swattn::make_plan(desc, n_q, window, SWATTN_MAX_PREFILL_NQ, &tmp);
     if (st == SWATTN_OK) *plan = tmp;
     return st;
 }
@@ -132,7 +147,7 @@ swattn_status_t swattn_plan(const swattn_desc_t* desc, int32_t n_q, int32_t wind
 swattn_status_t swattn_workspace_bytes(const swattn_desc_t* desc, int32_t n_q, int32_t window, size_t* bytes) {
     if (!bytes) return SWATTN_ERR_NULL;
     swattn_plan_t tmp;
-    swattn_status_t st = swattn::make_plan(desc, n_q, window, &tmp);
+    swattn_status_t st = swattn::make_plan(desc, n_q, window, SWATTN_MAX_NQ, &tmp);
     if (st == SWATTN_OK) *bytes = tmp.workspace_bytes;
     return st;
 }
@@ -142,7 +157,7 @@ const char* swattn_status_str(swattn_status_t s) {
         case SWATTN_OK: return "ok";
         case SWATTN_ERR_NULL: return "a required pointer is NULL";
         case SWATTN_ERR_SHAPE: return "invalid shape (batch, heads, head_dim, block sizes or max_ctx_len)";
-        case SWATTN_ERR_NQ: return "n_q outside [1, 64]";
+        case SWATTN_ERR_NQ: return "n_q outside [1, 64] (verify) or [1, 512] (prefill)";
         case SWATTN_ERR_WINDOW: return "window < 1";
         case SWATTN_ERR_DTYPE: return "unsupported dtype combination (or e4m3 KV without scales, or scales without e4m3)";
         case SWATTN_ERR_ALIGN: return "a data pointer is not 16-byte aligned";

@@ -217,6 +217,12 @@ def _c4(kv_dtype):
                          ctx_range=(188, 4096), max_blocks=256)
 
 
+def _prefill(n_q):
+    return make_workload(f"prefill_24layers_h8kv2_d256_bf16_ctx4096_w188_nq{n_q}", B=24, H=8, Hkv=2,
+                         D=256, n_q=n_q, window=188, ctx=4096, bs=16, seed=5,
+                         recent=188 + n_q - 1)
+
+
 # The five workloads of the build: tiny decode, single-stream verify, the
 # full-context split-KV contrast (three lengths), wide verify and the batched
 # stress test (fp8 and bf16 KV).
@@ -229,6 +235,7 @@ NAMED = {
     "wide_verify": _c3,
     "batched_fp8": lambda: _c4(E4M3),
     "batched_bf16": lambda: _c4(BF16),
+    "prefill_512": lambda: _prefill(512),
 }
 
 

@@ -129,6 +129,19 @@ def test_plan_variants_and_workspace():
     assert p.num_splits == 16
 
 
+def test_prefill_plan_caps_and_per_chunk_keys():
+    # n_q above 64 is for the prefill entry points only; 512 is their cap
+    assert sw.swattn_plan(desc(), 65, 188, check=False)[0] == -3
+    assert sw.swattn_prefill_plan(desc(), 65, 188).variant == sw.SWATTN_VARIANT_MFMA
+    assert sw.swattn_prefill_plan(desc(), 513, 188, check=False)[0] == -3
+    # a 32-row chunk of GQA-4 rows spans at most 9 queries: 188 + 8 keys, one split
+    p = sw.swattn_prefill_plan(desc(), 512, 188)
+    assert p.num_splits == 1 and p.row_chunks == 64 and p.workspace_bytes == 0
+    # full-context prefill: ceil(min(4096, 4096 + 8) / 512) = 8 splits
+    p = sw.swattn_prefill_plan(desc(), 512, 4096)
+    assert p.num_splits == 8 and p.merge_grid > 0
+
+
 def test_verify_host_checks_return_before_launch():
     lib = sw.lib()
     d = desc(num_splits=2)

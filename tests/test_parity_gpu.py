@@ -32,16 +32,16 @@ def _gpu():
 def test_named_workload(key):
     gu.log(f"[named] {key}")
     w, ref = gu.named(key)
-    got, plan = gu.run(w)
+    got, plan = gu.run(w, prefill=w.n_q > sw.SWATTN_MAX_NQ)
     gu.log(f"  plan {plan.as_dict()}")
     gu.check(got, ref, w.kv_dtype, out_f32=(w.q_dtype == "f32"), label=key)
 
 
-@pytest.mark.parametrize("key", ["verify", "wide_verify", "batched_fp8", "fullctx_2048"])
+@pytest.mark.parametrize("key", ["verify", "wide_verify", "batched_fp8", "fullctx_2048", "prefill_512"])
 def test_named_workload_f32_out(key):
     gu.log(f"[named f32 out] {key}")
     w, ref = gu.named(key)
-    got, _ = gu.run(w, out_f32=True)
+    got, _ = gu.run(w, out_f32=True, prefill=w.n_q > sw.SWATTN_MAX_NQ)
     gu.check(got, ref, w.kv_dtype, out_f32=True, label=key + "/f32")
 
 
@@ -208,6 +208,43 @@ def test_edge_shapes():
         got, plan = gu.run(w, out_f32=True)
         gu.log(f"  plan {plan.as_dict()}")
         gu.check(got, ref, w.kv_dtype, True, label=f"edge{k}")
+
+
+# ---------------------------------------------------------------------------
+# chunked prefill: n_q above the verify cap, same semantics
+# ---------------------------------------------------------------------------
+PREFILL_CASES = [
+    dict(B=1, H=8, Hkv=2, D=256, n_q=512, window=188, ctx=[4096], bs=16, S=0, kv="bf16", f32=False),
+    dict(B=2, H=4, Hkv=4, D=128, n_q=200, window=60, ctx=[700, 200], bs=16, S=3, kv="bf16", f32=True),
+    dict(B=1, H=8, Hkv=2, D=256, n_q=512, window=4096, ctx=[512], bs=16, S=0, kv="bf16", f32=True),
+    dict(B=2, H=8, Hkv=2, D=256, n_q=96, window=188, ctx=[1000, 300], bs=16, S=0, kv="e4m3", f32=False),
+    dict(B=1, H=6, Hkv=2, D=64, n_q=65, window=17, ctx=[65], bs=1, S=0, kv="bf16", f32=True),
+]
+
+
+@pytest.mark.parametrize("c", PREFILL_CASES, ids=lambda c: f"nq{c['n_q']}_W{c['window']}_{c['kv']}")
+def test_prefill_matches_oracle(c):
+    gu.log(f"[prefill] {c}")
+    w = synth.make_workload(f"pf{c['n_q']}", B=c["B"], H=c["H"], Hkv=c["Hkv"], D=c["D"], n_q=c["n_q"],
+                            window=c["window"], ctx=c["ctx"], bs=c["bs"], seed=40 + c["n_q"],
+                            kv_dtype=c["kv"], recent=c["window"] + c["n_q"] - 1)
+    ref = gu.reference(w)
+    got, plan = gu.run(w, out_f32=c["f32"], num_splits=c["S"], prefill=True)
+    gu.log(f"  plan {plan.as_dict()}")
+    gu.check(got, ref, w.kv_dtype, c["f32"], label=f"prefill n_q={c['n_q']}")
+
+
+def test_prefill_and_verify_agree_up_to_64_and_caps_differ():
+    w, _ = gu.named("verify")
+    t = gu.upload(w)
+    a, _ = gu.run(w, t=t, out_f32=True)
+    b, _ = gu.run(w, t=t, out_f32=True, prefill=True)
+    assert np.array_equal(a, b)
+    w65 = synth.make_workload("cap", B=1, H=8, Hkv=2, D=64, n_q=65, window=188, ctx=[300], bs=16, seed=13)
+    t65 = gu.upload(w65)
+    with pytest.raises(sw.SwattnError):
+        gu.run(w65, t=t65)
+    gu.run(w65, t=t65, prefill=True)
 
 
 # ---------------------------------------------------------------------------
