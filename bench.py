@@ -119,6 +119,96 @@ def cpu_baseline(w, budget_s):
             "sample": f"whole workload, {len(times)} run(s), median; float64 numpy, 1 BLAS thread"}
 
 
+def time_calls(torch, dev, stream, launch, flush, steps, with_graph):
+    """Per-call times of ``launch(stream_handle)`` (one library call):
+
+    cold_graph: ``steps`` calls captured in one HIP graph, each after an overwrite
+    of ``flush`` (512 MiB: twice the Infinity Cache), minus the same graph without
+    the calls, over ``steps`` (median of three replays); cold_eager: HIP events
+    around each eager call (adds dispatch latency); warm: back to back, and
+    replayed from a graph of 100 calls."""
+    def capture(with_calls):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            cs = torch.cuda.current_stream(dev).cuda_stream
+            for _ in range(steps):
+                flush.zero_()
+                if with_calls:
+                    launch(cs)
+        return g
+
+    g_pair, g_flush = capture(True), capture(False)
+    g_pair.replay()
+    g_flush.replay()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    per_call = []
+    wall = 0.0
+    for _ in range(3):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev[0].record(stream)
+        g_pair.replay()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        wall += time.perf_counter() - t0
+        ev[2].record(stream)
+        g_flush.replay()
+        ev[3].record(stream)
+        torch.cuda.synchronize()
+        per_call.append((ev[0].elapsed_time(ev[1]) - ev[2].elapsed_time(ev[3])) * 1e3 / steps)
+    cold_graph = statistics.median(per_call)
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        flush.zero_()
+        starts[i].record(stream)
+        launch(stream.cuda_stream)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    cold = sorted(s_.elapsed_time(e_) * 1e3 for s_, e_ in zip(starts, ends))   # us
+
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        launch(stream.cuda_stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    warm = e0.elapsed_time(e1) * 1e3 / steps
+
+    graph_us = None
+    if with_graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            cs = torch.cuda.current_stream(dev).cuda_stream
+            for _ in range(100):
+                launch(cs)
+        g.replay()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(5):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        graph_us = e0.elapsed_time(e1) * 1e3 / 500
+    return {
+        "cold_graph_us_per_call": round(cold_graph, 3),
+        "cold_graph_samples_us": [round(x, 3) for x in per_call],
+        "cold_eager_us_median": round(statistics.median(cold), 3),
+        "cold_eager_us_p10": round(cold[int(0.1 * (len(cold) - 1))], 3),
+        "cold_eager_us_p90": round(cold[int(0.9 * (len(cold) - 1))], 3),
+        "warm_us_back_to_back": round(warm, 3),
+        "graph_us_per_call_warm": None if graph_us is None else round(graph_us, 3),
+        "timed_region_wall_s": round(wall, 4),
+        "note": "value = cold_graph: K calls in one HIP graph, each after a 512 MiB overwrite, "
+                "minus the same graph without the calls, over K; cold_eager = HIP events around "
+                "each eager call (adds dispatch latency)",
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -129,6 +219,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--op", default="attention", choices=["attention", "append_kv"],
+                    help="attention: swattn_verify / swattn_prefill (default); append_kv: swattn_append_kv "
+                         "of the workload's new rows into its cache")
     ap.add_argument("--calibrate-copy", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -156,6 +249,10 @@ def main():
         print(json.dumps({"calibrate_copy_bytes": n}))
         return
 
+    if args.op == "append_kv":
+        run_append(args, torch, np, sw, synth, dev)
+        return
+
     w = synth.named_workload(args.workload)
 
     def to_dev(a, fmt):
@@ -180,15 +277,13 @@ def main():
     ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    def call():
-        call_lib(desc, q, k, v, bt, ctx, w.n_q, w.window, w.scale, out, ws,
-                         plan.workspace_bytes, stream.cuda_stream)
+    def launch(cs):
+        call_lib(desc, q, k, v, bt, ctx, w.n_q, w.window, w.scale, out, ws, plan.workspace_bytes, cs)
 
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-
     for _ in range(args.warmup):
         flush.zero_()
-        call()
+        launch(stream.cuda_stream)
     torch.cuda.synchronize()
 
     # Spot check against the oracle on a few sampled (layer, query, head) rows.
@@ -204,85 +299,8 @@ def main():
         worst = max(worst, float((np.abs(got[b:b + 1] - ref) - 1e-2 * np.abs(ref)).max()))
     parity_ok = worst <= (2e-2 if w.kv_dtype == "e4m3" else 2e-3)
 
-    # ---- cold-cache timed region: K calls captured in one HIP graph, each after a
-    # 512 MiB overwrite (twice the Infinity Cache); the same graph without the calls
-    # is timed too, and the per-call time is the difference over K.
-
-    def capture(with_calls):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            cs = torch.cuda.current_stream(dev).cuda_stream
-            for _ in range(args.steps):
-                flush.zero_()
-                if with_calls:
-                    call_lib(desc, q, k, v, bt, ctx, w.n_q, w.window, w.scale, out, ws,
-                                     plan.workspace_bytes, cs)
-        return g
-
-    g_pair, g_flush = capture(True), capture(False)
-    g_pair.replay()
-    g_flush.replay()
-    torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-    per_call = []
-    wall = 0.0
-    for _ in range(3):
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        ev[0].record(stream)
-        g_pair.replay()
-        ev[1].record(stream)
-        torch.cuda.synchronize()
-        wall += time.perf_counter() - t0
-        ev[2].record(stream)
-        g_flush.replay()
-        ev[3].record(stream)
-        torch.cuda.synchronize()
-        per_call.append((ev[0].elapsed_time(ev[1]) - ev[2].elapsed_time(ev[3])) * 1e3 / args.steps)
-    cold_graph = statistics.median(per_call)
-
-    # ---- cold, standalone: HIP events around each eager call (includes dispatch latency)
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        flush.zero_()
-        starts[i].record(stream)
-        call()
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    cold = sorted(s.elapsed_time(e) * 1e3 for s, e in zip(starts, ends))   # us
-    cold_med = statistics.median(cold)
-    cold_p10 = cold[int(0.1 * (len(cold) - 1))]
-    cold_p90 = cold[int(0.9 * (len(cold) - 1))]
-
-    # ---- warm, back to back ------------------------------------------------------------
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(args.steps):
-        call()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    warm = e0.elapsed_time(e1) * 1e3 / args.steps
-
-    # ---- one HIP graph of 100 calls, replayed (warm) -----------------------------------
-    graph_us = None
-    if not args.no_graph:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            cs = torch.cuda.current_stream(dev).cuda_stream
-            for _ in range(100):
-                call_lib(desc, q, k, v, bt, ctx, w.n_q, w.window, w.scale, out, ws,
-                                 plan.workspace_bytes, cs)
-        g.replay()
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(5):
-            g.replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        graph_us = e0.elapsed_time(e1) * 1e3 / 500
+    t = time_calls(torch, dev, stream, launch, flush, args.steps, not args.no_graph)
+    cold_graph = t["cold_graph_us_per_call"]
 
     nbytes = algorithmic_bytes(w)
     achieved = nbytes / (cold_graph * 1e-6) / 1e9
@@ -314,24 +332,90 @@ def main():
             "algorithmic_bytes": nbytes,
             "kernel": "partition" + ("" if plan.num_splits == 1 else "+merge"),
         },
-        "timing": {
-            "cold_graph_us_per_call": round(cold_graph, 3),
-            "cold_graph_samples_us": [round(x, 3) for x in per_call],
-            "cold_eager_us_median": round(cold_med, 3), "cold_eager_us_p10": round(cold_p10, 3),
-            "cold_eager_us_p90": round(cold_p90, 3),
-            "warm_us_back_to_back": round(warm, 3),
-            "graph_us_per_call_warm": None if graph_us is None else round(graph_us, 3),
-            "timed_region_wall_s": round(wall, 4),
-            "note": "value = cold_graph: K calls in one HIP graph, each after a 512 MiB overwrite, "
-                    "minus the same graph without the calls, over K; cold_eager = HIP events around "
-                    "each eager call (adds dispatch latency)",
-        },
+        "timing": t,
         "plan": plan.as_dict(),
         "parity_spot_check": {"ok": parity_ok, "worst_excess": worst},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+def run_append(args, torch, np, sw, synth, dev):
+    """swattn_append_kv of the workload's n_q new rows per sequence (bfloat16 K and V,
+    N(0,1)) into its paged cache (the workload's cache type: bfloat16, or E4M3 with its
+    per-head scales).  Same timing as the attention op; the written caches are compared
+    byte for byte with the oracle."""
+    import oracle
+    w = synth.named_workload(args.workload)
+    B, n, Hkv, D = w.B, w.n_q, w.Hkv, w.D
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((B, n, Hkv, D)).astype(np.float32)
+    kn, vn = oracle.f32_to_bf16_rne(x), oracle.f32_to_bf16_rne(-0.5 * x)
+
+    def dev_arr(a):
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
+
+    k, v = dev_arr(w.k_cache), dev_arr(w.v_cache)
+    kn_d, vn_d = dev_arr(kn), dev_arr(vn)
+    bt, ctx = dev_arr(w.block_table), dev_arr(w.ctx_len)
+    ks = None if w.k_scale is None else dev_arr(np.asarray(w.k_scale, np.float32))
+    vs = None if w.v_scale is None else dev_arr(np.asarray(w.v_scale, np.float32))
+    d = sw.swattn_desc_t()
+    d.batch, d.num_heads, d.num_kv_heads, d.head_dim = B, w.H, Hkv, D
+    d.block_size, d.max_blocks_per_seq, d.num_blocks = w.bs, w.block_table.shape[1], w.k_cache.shape[0]
+    d.max_ctx_len = int(w.ctx_len.max())
+    d.q_dtype, d.out_dtype = sw.SWATTN_BF16, sw.SWATTN_BF16
+    d.kv_dtype = {"bf16": sw.SWATTN_BF16, "e4m3": sw.SWATTN_FP8_E4M3, "f32": sw.SWATTN_F32}[w.kv_dtype]
+    d.k_scale = None if ks is None else ks.data_ptr()
+    d.v_scale = None if vs is None else vs.data_ptr()
+    stream = torch.cuda.current_stream(dev)
+
+    def launch(cs):
+        sw.swattn_append_kv(d, kn_d, vn_d, sw.SWATTN_BF16, bt, ctx, n, k, v, cs)
+
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    for _ in range(args.warmup):
+        launch(stream.cuda_stream)
+    torch.cuda.synchronize()
+    ek, ev = oracle.append_kv(w.k_cache, w.v_cache, w.block_table, w.ctx_len, kn, vn, n, new_format="bf16",
+                              kv_format=w.kv_format, k_scale=w.k_scale, v_scale=w.v_scale,
+                              max_ctx=int(w.ctx_len.max()))
+    gk, gv = k.cpu().numpy(), v.cpu().numpy()
+    parity_ok = (np.array_equal(gk.view(np.uint8), np.ascontiguousarray(ek).view(np.uint8)) and
+                 np.array_equal(gv.view(np.uint8), np.ascontiguousarray(ev).view(np.uint8)))
+
+    t = time_calls(torch, dev, stream, launch, flush, args.steps, not args.no_graph)
+    value = t["cold_graph_us_per_call"]
+    kv_elt = {"bf16": 2, "e4m3": 1, "f32": 4}[w.kv_dtype]
+    nbytes = 2 * B * n * Hkv * D * (2 + kv_elt)               # read the new rows, write the cache rows
+    achieved = nbytes / (value * 1e-6) / 1e9
+    line = {
+        "metric": "KV append us/call (n_new rows of every sequence into the paged cache)",
+        "value": value, "unit": "us/call", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(value / 1e3, 6), "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": f"bf16->{w.kv_dtype}", "data": "synthetic",
+        "config": {"workload": "KV append of the new rows of: " + DESCRIPTIONS.get(args.workload, w.name),
+                   "global_batch": B, "seq_len": int(w.ctx_len.max()), "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "algorithmic_bytes": nbytes,
+                     "kernel": "kv_append"},
+        "timing": t,
+        "parity_check": {"ok": bool(parity_ok), "what": "whole K and V caches, byte for byte, vs oracle.append_kv"},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        times = []
+        t_start = time.perf_counter()
+        while time.perf_counter() - t_start < args.cpu_budget and len(times) < 5:
+            t0 = time.perf_counter()
+            oracle.append_kv(w.k_cache, w.v_cache, w.block_table, w.ctx_len, kn, vn, n, new_format="bf16",
+                             kv_format=w.kv_format, k_scale=w.k_scale, v_scale=w.v_scale)
+            times.append(time.perf_counter() - t0)
+        line["cpu_baseline"] = {"value": round(statistics.median(times) * 1e6, 1), "unit": "us/call", "cores": 1,
+                                "kind": "oracle", "sample": f"whole workload, {len(times)} run(s), median"}
     print(json.dumps(line), flush=True)
 
 

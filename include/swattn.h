@@ -174,6 +174,43 @@ swattn_status_t swattn_prefill(const swattn_desc_t* desc,
                                void* stream);
 
 /*
+ * swattn_append_kv — write the n_new new K and V rows of every sequence into the
+ * paged cache, converting them to the cache's element type.
+ *
+ * Source: "The Fast Gemma Challenge: our verified-SOTA recipe, in full" (dev.to,
+ * VIDRAFT), full manifest.json — SPECULATIVE_CONFIG (a verify step scores the target
+ * token and 7 drafts, whose K/V rows must be in the cache before attention reads
+ * them) and section "What each piece does, and why" (decode is bound by the KV
+ * cache's bandwidth, which is why the cache may be stored in 8 bits).
+ *
+ *   k_new, v_new  [B][n_new][Hkv][D] new_dtype (F32 or BF16), device, read-only
+ *   block_table   [B][max_blocks_per_seq] int32, device
+ *   ctx_len       [B] int32, device; counts the new tokens, as in swattn_verify
+ *   k_cache, v_cache  [num_blocks][Hkv][block_size][D] desc->kv_dtype, device;
+ *                 only the new rows' positions are written
+ *
+ * Row (b, i, g) goes to position t = ctx_len[b] - n_new + i: block
+ * block_table[b][t / block_size], offset t % block_size.  Conversion to the cache
+ * type: bfloat16 rounds to nearest even; E4M3 stores the float32 quotient
+ * value / scale[g] (correctly rounded division, desc->k_scale / v_scale) rounded to
+ * the nearest E4M3 value, ties to the even code, saturating at +-448, NaN kept as
+ * NaN; float32 caches store the value.  desc fields used: batch, num_kv_heads,
+ * head_dim, block_size, max_blocks_per_seq, num_blocks, max_ctx_len, kv_dtype,
+ * k_scale, v_scale (the others are ignored).  n_new is in [1, SWATTN_MAX_PREFILL_NQ].
+ * A sequence whose ctx_len lies outside [n_new, min(max_ctx_len,
+ * max_blocks_per_seq*block_size)], or a position whose block id lies outside
+ * [0, num_blocks), is not written (nothing else is touched).  Host-checkable
+ * errors return before anything is enqueued; the call enqueues one kernel, never
+ * allocates or synchronises, and may be captured into a HIP graph.  Pointers as in
+ * swattn_verify (16-byte aligned data, 4-byte aligned tables).  The new rows must
+ * not overlap the cache.
+ */
+swattn_status_t swattn_append_kv(const swattn_desc_t* desc, const void* k_new, const void* v_new,
+                                 swattn_dtype_t new_dtype, const int32_t* block_table,
+                                 const int32_t* ctx_len, int32_t n_new, void* k_cache, void* v_cache,
+                                 void* stream);
+
+/*
  * swattn_check_inputs — debug check of the device-resident preconditions (n_q up to
  * SWATTN_MAX_PREFILL_NQ).  Copies ctx_len and block_table to the host (synchronising the stream) and
  * returns SWATTN_ERR_CTX if some ctx_len[b] lies outside

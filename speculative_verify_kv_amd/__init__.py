@@ -4,7 +4,8 @@ Argument marshalling only: every step of the computation runs in the HIP
 kernels of ``libswattn.so``.  The functions mirror the C ABI in
 ``include/swattn.h`` one for one (``swattn_plan``, ``swattn_workspace_bytes``,
 ``swattn_verify``, ``swattn_prefill_plan``, ``swattn_prefill``,
-``swattn_check_inputs``, ``swattn_status_str``, ``swattn_abi_version``);
+``swattn_append_kv``, ``swattn_check_inputs``, ``swattn_status_str``,
+``swattn_abi_version``);
 ``verify`` and ``prefill`` are conveniences that fill the descriptor from torch
 tensors and run on torch's current HIP stream.  There is no CPU
 fallback: if the library is missing, loading fails with an error.
@@ -29,7 +30,8 @@ STATUS = {
 
 # Symbols declared in include/swattn.h.
 EXPORTED = ("swattn_plan", "swattn_workspace_bytes", "swattn_verify", "swattn_prefill_plan",
-            "swattn_prefill", "swattn_check_inputs", "swattn_status_str", "swattn_abi_version")
+            "swattn_prefill", "swattn_append_kv", "swattn_check_inputs", "swattn_status_str",
+            "swattn_abi_version")
 
 
 class SwattnError(RuntimeError):
@@ -94,6 +96,10 @@ def lib():
         L.swattn_prefill_plan.restype = ctypes.c_int
         L.swattn_prefill.argtypes = L.swattn_verify.argtypes
         L.swattn_prefill.restype = ctypes.c_int
+        L.swattn_append_kv.argtypes = [P(swattn_desc_t), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_void_p]
+        L.swattn_append_kv.restype = ctypes.c_int
         L.swattn_check_inputs.argtypes = [P(swattn_desc_t), ctypes.c_void_p, ctypes.c_void_p,
                                           ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
         L.swattn_check_inputs.restype = ctypes.c_int
@@ -165,6 +171,16 @@ def swattn_prefill(desc, q, k_cache, v_cache, block_table, ctx_len, n_q, window,
                               _ptr(stream))
     if check and st != 0:
         raise SwattnError(st, "swattn_prefill")
+    return st
+
+
+def swattn_append_kv(desc, k_new, v_new, new_dtype, block_table, ctx_len, n_new, k_cache, v_cache,
+                     stream=None, check=True):
+    st = lib().swattn_append_kv(ctypes.byref(desc), _ptr(k_new), _ptr(v_new), int(new_dtype),
+                                _ptr(block_table), _ptr(ctx_len), int(n_new), _ptr(k_cache), _ptr(v_cache),
+                                _ptr(stream))
+    if check and st != 0:
+        raise SwattnError(st, "swattn_append_kv")
     return st
 
 

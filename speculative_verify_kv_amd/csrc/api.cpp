@@ -167,3 +167,54 @@ extern "C" swattn_status_t swattn_check_inputs(const swattn_desc_t* d, const int
     }
     return SWATTN_OK;
 }
+
+extern "C" swattn_status_t swattn_append_kv(const swattn_desc_t* d, const void* k_new, const void* v_new,
+                                            swattn_dtype_t new_dtype, const int32_t* block_table,
+                                            const int32_t* ctx_len, int32_t n_new, void* k_cache, void* v_cache,
+                                            void* stream) {
+    using namespace swattn;
+    if (!d) return SWATTN_ERR_NULL;
+    if (d->batch < 1 || d->num_kv_heads < 1) return SWATTN_ERR_SHAPE;
+    if (d->head_dim != 64 && d->head_dim != 128 && d->head_dim != 256) return SWATTN_ERR_SHAPE;
+    if (d->block_size < 1 || d->max_blocks_per_seq < 1 || d->num_blocks < 1 || d->max_ctx_len < 1)
+        return SWATTN_ERR_SHAPE;
+    if ((int64_t)d->max_ctx_len > (int64_t)d->max_blocks_per_seq * d->block_size) return SWATTN_ERR_SHAPE;
+    if ((int64_t)d->num_blocks * d->num_kv_heads * d->block_size > INT32_MAX) return SWATTN_ERR_SHAPE;
+    if ((int64_t)d->max_blocks_per_seq * d->block_size > INT32_MAX) return SWATTN_ERR_SHAPE;
+    if (n_new < 1 || n_new > SWATTN_MAX_PREFILL_NQ) return SWATTN_ERR_NQ;
+    if (new_dtype != SWATTN_F32 && new_dtype != SWATTN_BF16) return SWATTN_ERR_DTYPE;
+    if (d->kv_dtype != SWATTN_F32 && d->kv_dtype != SWATTN_BF16 && d->kv_dtype != SWATTN_FP8_E4M3)
+        return SWATTN_ERR_DTYPE;
+    const bool fp8 = d->kv_dtype == SWATTN_FP8_E4M3;
+    if (fp8 && (!d->k_scale || !d->v_scale)) return SWATTN_ERR_DTYPE;
+    if (!fp8 && (d->k_scale || d->v_scale)) return SWATTN_ERR_DTYPE;
+    if (!k_new || !v_new || !block_table || !ctx_len || !k_cache || !v_cache) return SWATTN_ERR_NULL;
+    if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+        !aligned(block_table, 4) || !aligned(ctx_len, 4))
+        return SWATTN_ERR_ALIGN;
+    if (fp8 && (!aligned(d->k_scale, 4) || !aligned(d->v_scale, 4))) return SWATTN_ERR_ALIGN;
+    const int64_t threads = 2 * (int64_t)d->batch * n_new * d->num_kv_heads * (d->head_dim / 8);
+    const int64_t grid = (threads + kBlockThreads - 1) / kBlockThreads;
+    if (grid > INT32_MAX) return SWATTN_ERR_SHAPE;
+
+    AppendParams p;
+    p.k_new = k_new;
+    p.v_new = v_new;
+    p.k_cache = k_cache;
+    p.v_cache = v_cache;
+    p.block_table = block_table;
+    p.ctx_len = ctx_len;
+    p.k_scale = d->k_scale;
+    p.v_scale = d->v_scale;
+    p.B = d->batch;
+    p.Hkv = d->num_kv_heads;
+    p.D = d->head_dim;
+    p.bs = d->block_size;
+    p.max_blocks = d->max_blocks_per_seq;
+    p.num_blocks = d->num_blocks;
+    p.max_ctx = d->max_ctx_len;
+    p.n_new = n_new;
+    p.new_dtype = new_dtype;
+    p.kv_dtype = d->kv_dtype;
+    return launch_kv_append(p, (int)grid, stream) == 0 ? SWATTN_OK : SWATTN_ERR_HIP;
+}

@@ -45,6 +45,20 @@ struct MergeParams {
     int32_t out_dtype;
 };
 
+// KV-cache append (kv_append.hip).
+struct AppendParams {
+    const void* k_new;    // [B][n_new][Hkv][D] new_dtype
+    const void* v_new;
+    void* k_cache;        // [num_blocks][Hkv][bs][D] kv_dtype
+    void* v_cache;
+    const int32_t* block_table;
+    const int32_t* ctx_len;
+    const float* k_scale;
+    const float* v_scale;
+    int32_t B, Hkv, D, bs, max_blocks, num_blocks, max_ctx, n_new;
+    int32_t new_dtype, kv_dtype;
+};
+
 // Geometry helpers used by both the planner and the host launch code.
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
@@ -52,5 +66,6 @@ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 int launch_partition_mfma(const PartitionParams& p, int grid, void* stream);
 int launch_partition_valu(const PartitionParams& p, int grid, void* stream);
 int launch_merge(const MergeParams& p, int grid, void* stream);
+int launch_kv_append(const AppendParams& p, int grid, void* stream);
 
 }  // namespace swattn
