@@ -22,12 +22,15 @@ closed forms (K = 0 gives a moving average, two-key sigmoid, constant V),
 hand-derived fixtures under tests/golden/, and every e4m3 / bf16 code against
 torch's own conversions; for the KV append (kv_append.py), E4M3 and bfloat16
 rounding against torch's casts and hand-derived cases, and the write pattern
-against a dense per-position reference.  No function here is "parity unpinned".
+against a dense per-position reference; for the greedy acceptance (accept.py),
+hand-built acceptance patterns and the argmax against a sorting definition.
+No function here is "parity unpinned".
 """
 from .formats import decode_e4m3, decode_bf16, e4m3_value_table
 from .attend import attend, attend_bruteforce, window_bounds
 from .splitmerge import attend_split_merge
 from .kv_append import append_kv, quantize_e4m3, f32_to_bf16_rne
+from .accept import greedy_accept, row_argmax
 
 __all__ = [
     "decode_e4m3",
@@ -40,4 +43,6 @@ __all__ = [
     "append_kv",
     "quantize_e4m3",
     "f32_to_bf16_rne",
+    "greedy_accept",
+    "row_argmax",
 ]
