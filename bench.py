@@ -219,9 +219,11 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
-    ap.add_argument("--op", default="attention", choices=["attention", "append_kv"],
+    ap.add_argument("--op", default="attention", choices=["attention", "append_kv", "accept"],
                     help="attention: swattn_verify / swattn_prefill (default); append_kv: swattn_append_kv "
-                         "of the workload's new rows into its cache")
+                         "of the workload's new rows into its cache; accept: swattn_greedy_accept")
+    ap.add_argument("--vocab", type=int, default=262144, help="accept op: logits per position")
+    ap.add_argument("--accept-batch", type=int, default=1, help="accept op: sequences per call")
     ap.add_argument("--calibrate-copy", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -251,6 +253,9 @@ def main():
 
     if args.op == "append_kv":
         run_append(args, torch, np, sw, synth, dev)
+        return
+    if args.op == "accept":
+        run_accept(args, torch, np, sw, dev)
         return
 
     w = synth.named_workload(args.workload)
@@ -413,6 +418,73 @@ def run_append(args, torch, np, sw, synth, dev):
             t0 = time.perf_counter()
             oracle.append_kv(w.k_cache, w.v_cache, w.block_table, w.ctx_len, kn, vn, n, new_format="bf16",
                              kv_format=w.kv_format, k_scale=w.k_scale, v_scale=w.v_scale)
+            times.append(time.perf_counter() - t0)
+        line["cpu_baseline"] = {"value": round(statistics.median(times) * 1e6, 1), "unit": "us/call", "cores": 1,
+                                "kind": "oracle", "sample": f"whole workload, {len(times)} run(s), median"}
+    print(json.dumps(line), flush=True)
+
+
+def run_accept(args, torch, np, sw, dev):
+    """swattn_greedy_accept on one verify step's target logits: --accept-batch sequences
+    x 8 positions x --vocab bfloat16 logits ~ N(0, 1), seed 6, with drafts that agree
+    with the target for a random prefix.  Same timing as the attention op; the outputs
+    are compared exactly with the oracle."""
+    import oracle
+    B, n_q, vocab = args.accept_batch, 8, args.vocab
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((B, n_q, vocab)).astype(np.float32)
+    bits = oracle.f32_to_bf16_rne(x)
+    vals = (bits.astype(np.uint32) << 16).view(np.float32)
+    target = oracle.row_argmax(vals)
+    drafts = target[:, :n_q - 1].astype(np.int32).copy()
+    cut = rng.integers(0, n_q, B)
+    for b in range(B):
+        if cut[b] < n_q - 1:
+            drafts[b, cut[b]] = (drafts[b, cut[b]] + 1) % vocab
+    logits = torch.from_numpy(bits.view(np.int16)).to(dev)
+    d = torch.from_numpy(drafts).to(dev)
+    tgt = torch.empty((B, n_q), dtype=torch.int32, device=dev)
+    acc = torch.empty((B,), dtype=torch.int32, device=dev)
+    nxt = torch.empty((B,), dtype=torch.int32, device=dev)
+    nbytes_ws = sw.swattn_greedy_accept_workspace(B, n_q, vocab)
+    ws = torch.empty(max(nbytes_ws, 8) // 8, dtype=torch.int64, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def launch(cs):
+        sw.swattn_greedy_accept(logits, sw.SWATTN_BF16, B, n_q, vocab, d, tgt, acc, nxt, ws, ws.numel() * 8, cs)
+
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    for _ in range(args.warmup):
+        launch(stream.cuda_stream)
+    torch.cuda.synchronize()
+    et, ea, en = oracle.greedy_accept(vals, drafts)
+    parity_ok = (np.array_equal(tgt.cpu().numpy(), et) and np.array_equal(acc.cpu().numpy(), ea)
+                 and np.array_equal(nxt.cpu().numpy(), en))
+    t = time_calls(torch, dev, stream, launch, flush, args.steps, not args.no_graph)
+    value = t["cold_graph_us_per_call"]
+    nbytes = B * n_q * vocab * 2 + B * (n_q - 1) * 4 + B * n_q * 4 + 2 * B * 4
+    achieved = nbytes / (value * 1e-6) / 1e9
+    line = {
+        "metric": "greedy acceptance us/call (argmax of every position's logits + accepted drafts)",
+        "value": value, "unit": "us/call", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(value / 1e3, 6), "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"greedy acceptance: {B} sequence(s) x {n_q} positions x {vocab} bf16 logits "
+                               "~ N(0,1), drafts agree for a random prefix, seed 6",
+                   "global_batch": B, "seq_len": n_q, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "algorithmic_bytes": nbytes,
+                     "kernel": "argmax_chunks+accept_finalize"},
+        "timing": t,
+        "parity_check": {"ok": bool(parity_ok), "what": "target ids, accepted counts, next tokens vs oracle"},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        times = []
+        t_start = time.perf_counter()
+        while time.perf_counter() - t_start < args.cpu_budget and len(times) < 20:
+            t0 = time.perf_counter()
+            oracle.greedy_accept(vals, drafts)
             times.append(time.perf_counter() - t0)
         line["cpu_baseline"] = {"value": round(statistics.median(times) * 1e6, 1), "unit": "us/call", "cores": 1,
                                 "kind": "oracle", "sample": f"whole workload, {len(times)} run(s), median"}

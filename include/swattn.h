@@ -211,6 +211,40 @@ swattn_status_t swattn_append_kv(const swattn_desc_t* desc, const void* k_new, c
                                  void* stream);
 
 /*
+ * swattn_greedy_accept — greedy acceptance of one verify step's drafts.
+ *
+ * Source: "The Fast Gemma Challenge: our verified-SOTA recipe, in full" (dev.to,
+ * VIDRAFT), full manifest.json — OVERRIDE_GENERATION_CONFIG (temperature 0, top_p 1,
+ * top_k 0: greedy generation, so the target's token is the argmax of its logits),
+ * SPECULATIVE_CONFIG (a verify step scores the last accepted token and 7 drafts) and
+ * FUSED_SPARSE_ARGMAX (the argmax is fused into the step instead of sampled).
+ *
+ *   logits      [B][n_q][vocab] logits_dtype (F32 or BF16), device, read-only; the
+ *               target's logits after each of the step's n_q inputs
+ *   draft_ids   [B][n_q - 1] int32, device; draft_ids[b][j] is the drafter's guess for
+ *               the token after input j (may be NULL when n_q == 1)
+ *   target_ids  [B][n_q] int32, device, written: argmax_v logits[b][i][v], the lowest
+ *               index among equal maxima; a NaN counts as larger than every number (the
+ *               first NaN wins); -0 equals +0
+ *   accepted    [B] int32, device, written: the largest a <= n_q - 1 such that
+ *               draft_ids[b][j] == target_ids[b][j] for every j < a
+ *   next_token  [B] int32, device, written: target_ids[b][accepted[b]]
+ *   workspace   device scratch of >= swattn_greedy_accept_workspace(B, n_q, vocab) bytes,
+ *               8-byte aligned; contents undefined afterwards
+ *
+ * n_q in [1, SWATTN_MAX_NQ], vocab >= 1.  logits aligned to its element size.  Two
+ * kernels on the stream (a chunked argmax and a per-sequence finalize); no
+ * allocation or synchronisation, capturable into a HIP graph.  Host-checkable errors
+ * return before anything is enqueued.
+ */
+swattn_status_t swattn_greedy_accept_workspace(int32_t batch, int32_t n_q, int32_t vocab, size_t* bytes);
+
+swattn_status_t swattn_greedy_accept(const void* logits, swattn_dtype_t logits_dtype, int32_t batch,
+                                     int32_t n_q, int32_t vocab, const int32_t* draft_ids,
+                                     int32_t* target_ids, int32_t* accepted, int32_t* next_token,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * swattn_check_inputs — debug check of the device-resident preconditions (n_q up to
  * SWATTN_MAX_PREFILL_NQ).  Copies ctx_len and block_table to the host (synchronising the stream) and
  * returns SWATTN_ERR_CTX if some ctx_len[b] lies outside

@@ -4,7 +4,8 @@ Argument marshalling only: every step of the computation runs in the HIP
 kernels of ``libswattn.so``.  The functions mirror the C ABI in
 ``include/swattn.h`` one for one (``swattn_plan``, ``swattn_workspace_bytes``,
 ``swattn_verify``, ``swattn_prefill_plan``, ``swattn_prefill``,
-``swattn_append_kv``, ``swattn_check_inputs``, ``swattn_status_str``,
+``swattn_append_kv``, ``swattn_greedy_accept_workspace``,
+``swattn_greedy_accept``, ``swattn_check_inputs``, ``swattn_status_str``,
 ``swattn_abi_version``);
 ``verify`` and ``prefill`` are conveniences that fill the descriptor from torch
 tensors and run on torch's current HIP stream.  There is no CPU
@@ -30,8 +31,8 @@ STATUS = {
 
 # Symbols declared in include/swattn.h.
 EXPORTED = ("swattn_plan", "swattn_workspace_bytes", "swattn_verify", "swattn_prefill_plan",
-            "swattn_prefill", "swattn_append_kv", "swattn_check_inputs", "swattn_status_str",
-            "swattn_abi_version")
+            "swattn_prefill", "swattn_append_kv", "swattn_greedy_accept_workspace",
+            "swattn_greedy_accept", "swattn_check_inputs", "swattn_status_str", "swattn_abi_version")
 
 
 class SwattnError(RuntimeError):
@@ -100,6 +101,13 @@ def lib():
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
                                        ctypes.c_void_p, ctypes.c_void_p]
         L.swattn_append_kv.restype = ctypes.c_int
+        L.swattn_greedy_accept_workspace.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                     P(ctypes.c_size_t)]
+        L.swattn_greedy_accept_workspace.restype = ctypes.c_int
+        L.swattn_greedy_accept.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int32, ctypes.c_int32,
+                                           ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        L.swattn_greedy_accept.restype = ctypes.c_int
         L.swattn_check_inputs.argtypes = [P(swattn_desc_t), ctypes.c_void_p, ctypes.c_void_p,
                                           ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
         L.swattn_check_inputs.restype = ctypes.c_int
@@ -182,6 +190,42 @@ def swattn_append_kv(desc, k_new, v_new, new_dtype, block_table, ctx_len, n_new,
     if check and st != 0:
         raise SwattnError(st, "swattn_append_kv")
     return st
+
+
+def swattn_greedy_accept_workspace(batch, n_q, vocab):
+    n = ctypes.c_size_t(0)
+    st = lib().swattn_greedy_accept_workspace(int(batch), int(n_q), int(vocab), ctypes.byref(n))
+    if st != 0:
+        raise SwattnError(st, "swattn_greedy_accept_workspace")
+    return int(n.value)
+
+
+def swattn_greedy_accept(logits, logits_dtype, batch, n_q, vocab, draft_ids, target_ids, accepted, next_token,
+                         workspace, workspace_bytes, stream=None, check=True):
+    st = lib().swattn_greedy_accept(_ptr(logits), int(logits_dtype), int(batch), int(n_q), int(vocab),
+                                    _ptr(draft_ids), _ptr(target_ids), _ptr(accepted), _ptr(next_token),
+                                    _ptr(workspace), int(workspace_bytes), _ptr(stream))
+    if check and st != 0:
+        raise SwattnError(st, "swattn_greedy_accept")
+    return st
+
+
+def greedy_accept(logits, draft_ids, stream=None):
+    """Run swattn_greedy_accept on torch device tensors (logits [B, n_q, vocab] float32
+    or bfloat16, draft_ids [B, n_q - 1] int32); returns (target_ids, accepted, next_token)."""
+    import torch
+    B, n_q, vocab = logits.shape
+    code = SWATTN_BF16 if logits.dtype == torch.bfloat16 else SWATTN_F32
+    tgt = torch.empty((B, n_q), dtype=torch.int32, device=logits.device)
+    acc = torch.empty((B,), dtype=torch.int32, device=logits.device)
+    nxt = torch.empty((B,), dtype=torch.int32, device=logits.device)
+    nbytes = swattn_greedy_accept_workspace(B, n_q, vocab)
+    ws = torch.empty(max(nbytes, 8) // 8, dtype=torch.int64, device=logits.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(logits.device).cuda_stream
+    swattn_greedy_accept(logits, code, B, n_q, vocab, draft_ids if n_q > 1 else None, tgt, acc, nxt, ws,
+                         ws.numel() * 8, stream)
+    return tgt, acc, nxt
 
 
 def swattn_check_inputs(desc, block_table, ctx_len, n_q, window, stream=None):

@@ -18,7 +18,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libswattn.so")
 ARCH = "gfx950"
 
-SOURCES = ["plan.cpp", "api.cpp", "partition_mfma.hip", "partition_valu.hip", "merge.hip", "kv_append.hip"]
+SOURCES = ["plan.cpp", "api.cpp", "partition_mfma.hip", "partition_valu.hip", "merge.hip", "kv_append.hip",
+           "accept.hip"]
 
 # hipcc's host pass does not know this target feature and says so; harmless.
 # It keeps the device compiler from forming packed-fp32 instructions.

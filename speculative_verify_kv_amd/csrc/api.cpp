@@ -218,3 +218,64 @@ extern "C" swattn_status_t swattn_append_kv(const swattn_desc_t* d, const void* 
     p.kv_dtype = d->kv_dtype;
     return launch_kv_append(p, (int)grid, stream) == 0 ? SWATTN_OK : SWATTN_ERR_HIP;
 }
+
+namespace swattn {
+namespace {
+
+swattn_status_t accept_shape(int32_t batch, int32_t n_q, int32_t vocab, int64_t* nchunk, size_t* bytes) {
+    if (batch < 1 || vocab < 1) return SWATTN_ERR_SHAPE;
+    if (n_q < 1 || n_q > SWATTN_MAX_NQ) return SWATTN_ERR_NQ;
+    const int64_t nc = ((int64_t)vocab + kAcceptChunk - 1) / kAcceptChunk;
+    if ((int64_t)batch * n_q * nc > INT32_MAX) return SWATTN_ERR_SHAPE;
+    *nchunk = nc;
+    *bytes = (size_t)((int64_t)batch * n_q * nc * 8);
+    return SWATTN_OK;
+}
+
+}  // namespace
+}  // namespace swattn
+
+extern "C" swattn_status_t swattn_greedy_accept_workspace(int32_t batch, int32_t n_q, int32_t vocab,
+                                                          size_t* bytes) {
+    if (!bytes) return SWATTN_ERR_NULL;
+    int64_t nc;
+    size_t b;
+    const swattn_status_t st = swattn::accept_shape(batch, n_q, vocab, &nc, &b);
+    if (st == SWATTN_OK) *bytes = b;
+    return st;
+}
+
+extern "C" swattn_status_t swattn_greedy_accept(const void* logits, swattn_dtype_t logits_dtype, int32_t batch,
+                                                int32_t n_q, int32_t vocab, const int32_t* draft_ids,
+                                                int32_t* target_ids, int32_t* accepted, int32_t* next_token,
+                                                void* workspace, size_t workspace_bytes, void* stream) {
+    using namespace swattn;
+    int64_t nchunk;
+    size_t need;
+    swattn_status_t st = accept_shape(batch, n_q, vocab, &nchunk, &need);
+    if (st != SWATTN_OK) return st;
+    if (logits_dtype != SWATTN_F32 && logits_dtype != SWATTN_BF16) return SWATTN_ERR_DTYPE;
+    if (!logits || !target_ids || !accepted || !next_token || (n_q > 1 && !draft_ids)) return SWATTN_ERR_NULL;
+    if (!workspace || workspace_bytes < need) return SWATTN_ERR_WORKSPACE;
+    const uintptr_t elt = logits_dtype == SWATTN_F32 ? 4 : 2;
+    if (!aligned(logits, elt) || !aligned(workspace, 8) || !aligned(target_ids, 4) || !aligned(accepted, 4) ||
+        !aligned(next_token, 4) || (draft_ids && !aligned(draft_ids, 4)))
+        return SWATTN_ERR_ALIGN;
+    AcceptParams p;
+    p.logits = logits;
+    p.draft_ids = draft_ids;
+    p.target_ids = target_ids;
+    p.accepted = accepted;
+    p.next_token = next_token;
+    p.partial = reinterpret_cast<uint64_t*>(workspace);
+    p.B = batch;
+    p.n_q = n_q;
+    p.vocab = vocab;
+    p.nchunk = (int32_t)nchunk;
+    p.logits_dtype = logits_dtype;
+    // 16-byte loads when every row starts 16-byte aligned
+    const int64_t per_load = 16 / (int64_t)elt;
+    p.vec_ok = aligned(logits, 16) && vocab % per_load == 0;
+    const int64_t grid1 = (int64_t)batch * n_q * nchunk;
+    return launch_accept(p, (int)grid1, stream) == 0 ? SWATTN_OK : SWATTN_ERR_HIP;
+}

@@ -59,6 +59,19 @@ struct AppendParams {
     int32_t new_dtype, kv_dtype;
 };
 
+// Greedy acceptance (accept.hip).
+constexpr int kAcceptChunk = 8192;           // logits per workgroup of the argmax pass
+constexpr int kAcceptMaxNq = 64;             // positions per sequence (the verify cap)
+struct AcceptParams {
+    const void* logits;   // [B][n_q][vocab] float32 or bfloat16
+    const int32_t* draft_ids;   // [B][n_q - 1]
+    int32_t* target_ids;        // [B][n_q]
+    int32_t* accepted;          // [B]
+    int32_t* next_token;        // [B]
+    uint64_t* partial;          // [B * n_q][nchunk] argmax keys (workspace)
+    int32_t B, n_q, vocab, nchunk, logits_dtype, vec_ok;
+};
+
 // Geometry helpers used by both the planner and the host launch code.
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
@@ -67,5 +80,6 @@ int launch_partition_mfma(const PartitionParams& p, int grid, void* stream);
 int launch_partition_valu(const PartitionParams& p, int grid, void* stream);
 int launch_merge(const MergeParams& p, int grid, void* stream);
 int launch_kv_append(const AppendParams& p, int grid, void* stream);
+int launch_accept(const AcceptParams& p, int grid1, void* stream);
 
 }  // namespace swattn
