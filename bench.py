@@ -219,9 +219,10 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
-    ap.add_argument("--op", default="attention", choices=["attention", "append_kv", "accept"],
+    ap.add_argument("--op", default="attention", choices=["attention", "append_kv", "accept", "layer_graph"],
                     help="attention: swattn_verify / swattn_prefill (default); append_kv: swattn_append_kv "
-                         "of the workload's new rows into its cache; accept: swattn_greedy_accept")
+                         "of the workload's new rows into its cache; accept: swattn_greedy_accept; "
+                         "layer_graph: one decode step as a graph of per-layer calls")
     ap.add_argument("--vocab", type=int, default=262144, help="accept op: logits per position")
     ap.add_argument("--accept-batch", type=int, default=1, help="accept op: sequences per call")
     ap.add_argument("--calibrate-copy", type=int, default=0,
@@ -256,6 +257,9 @@ def main():
         return
     if args.op == "accept":
         run_accept(args, torch, np, sw, dev)
+        return
+    if args.op == "layer_graph":
+        run_layer_graph(args, torch, np, sw, synth, dev)
         return
 
     w = synth.named_workload(args.workload)
@@ -488,6 +492,131 @@ def run_accept(args, torch, np, sw, dev):
             times.append(time.perf_counter() - t0)
         line["cpu_baseline"] = {"value": round(statistics.median(times) * 1e6, 1), "unit": "us/call", "cores": 1,
                                 "kind": "oracle", "sample": f"whole workload, {len(times)} run(s), median"}
+    print(json.dumps(line), flush=True)
+
+
+def run_layer_graph(args, torch, np, sw, synth, dev):
+    """One decode step of the verify workload's 24 layers as a model runs it: per layer,
+    swattn_append_kv of the layer's 8 new K/V rows then swattn_verify of that layer
+    alone (B = 1), and at the end swattn_greedy_accept on the step's logits (8 x
+    --vocab bf16).  The step is captured into one HIP graph per buffer slot (3 slots,
+    graphs replayed round-robin, 20 warm-up replays each, after the manifest's
+    LOOPGRAPH_PINGPONG_SLOTS / LOOPGRAPH_WARMUP_CALLS), and compared with the same step
+    issued as three stacked calls (all layers in one append and one verify call).
+    Outputs of both forms must be equal bit for bit."""
+    import oracle
+    w = synth.named_workload("verify")
+    L, n, H, Hkv, D = w.B, w.n_q, w.H, w.Hkv, w.D
+    vocab, n_slots = args.vocab, 3
+    rng = np.random.default_rng(8)
+
+    def bf16_dev(x32):
+        return torch.from_numpy(oracle.f32_to_bf16_rne(x32).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    k = torch.from_numpy(np.ascontiguousarray(w.k_cache).view(np.int16)).to(dev).view(torch.bfloat16)
+    v = torch.from_numpy(np.ascontiguousarray(w.v_cache).view(np.int16)).to(dev).view(torch.bfloat16)
+    bt = torch.from_numpy(w.block_table).to(dev)
+    ctx = torch.from_numpy(w.ctx_len).to(dev)
+    max_ctx = int(w.ctx_len.max())
+    slots = []
+    for s_ in range(n_slots):
+        slot = dict(
+            q=bf16_dev(rng.standard_normal((L, n, H, D)).astype(np.float32)),
+            kn=bf16_dev(rng.standard_normal((L, n, Hkv, D)).astype(np.float32)),
+            vn=bf16_dev(rng.standard_normal((L, n, Hkv, D)).astype(np.float32)),
+            logits=bf16_dev(rng.standard_normal((1, n, vocab)).astype(np.float32)),
+            drafts=torch.from_numpy(rng.integers(0, vocab, (1, n - 1)).astype(np.int32)).to(dev))
+        for form in ("layers", "stacked"):
+            slot[form] = dict(out=torch.empty((L, n, H, D), dtype=torch.bfloat16, device=dev),
+                              tgt=torch.empty((1, n), dtype=torch.int32, device=dev),
+                              acc=torch.empty((1,), dtype=torch.int32, device=dev),
+                              nxt=torch.empty((1,), dtype=torch.int32, device=dev))
+        slots.append(slot)
+    ws_acc = torch.empty(sw.swattn_greedy_accept_workspace(1, n, vocab) // 8 + 1, dtype=torch.int64, device=dev)
+    desc_all = sw.make_desc(slots[0]["q"], k, bt, max_ctx)
+    desc_l = [sw.make_desc(slots[0]["q"][l:l + 1], k, bt[l:l + 1], max_ctx, num_splits=args.splits)
+              for l in range(L)]
+    plan_l = sw.swattn_plan(desc_l[0], n, w.window)
+    plan_all = sw.swattn_plan(desc_all, n, w.window)
+    assert plan_all.workspace_bytes == 0
+    # the per-layer calls run one after another on the stream: one workspace serves them all
+    ws_l = torch.empty(max(plan_l.workspace_bytes, 256), dtype=torch.uint8, device=dev)
+
+    def step(slot, form, cs):
+        o = slot[form]
+        if form == "layers":
+            for l in range(L):
+                sw.swattn_append_kv(desc_l[l], slot["kn"][l:l + 1], slot["vn"][l:l + 1], sw.SWATTN_BF16,
+                                    bt[l:l + 1], ctx[l:l + 1], n, k, v, cs)
+                sw.swattn_verify(desc_l[l], slot["q"][l:l + 1], k, v, bt[l:l + 1], ctx[l:l + 1], n, w.window,
+                                 w.scale, o["out"][l:l + 1], ws_l, plan_l.workspace_bytes, cs)
+        else:
+            sw.swattn_append_kv(desc_all, slot["kn"], slot["vn"], sw.SWATTN_BF16, bt, ctx, n, k, v, cs)
+            sw.swattn_verify(desc_all, slot["q"], k, v, bt, ctx, n, w.window, w.scale, o["out"], None, 0, cs)
+        sw.swattn_greedy_accept(slot["logits"], sw.SWATTN_BF16, 1, n, vocab, slot["drafts"], o["tgt"], o["acc"],
+                                o["nxt"], ws_acc, ws_acc.numel() * 8, cs)
+
+    stream = torch.cuda.current_stream(dev)
+    graphs = {}
+    for form in ("layers", "stacked"):
+        graphs[form] = []
+        for slot in slots:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(slot, form, torch.cuda.current_stream(dev).cuda_stream)
+            graphs[form].append(g)
+    for form in graphs:
+        for _ in range(20):
+            for g in graphs[form]:
+                g.replay()
+    torch.cuda.synchronize()
+    if plan_l.num_splits == plan_all.num_splits:
+        same = all(torch.equal(sl["layers"][key], sl["stacked"][key]) for sl in slots
+                   for key in ("out", "tgt", "acc", "nxt"))
+    else:   # other split counts round differently: outputs within the verify tolerance, ids equal
+        same = all(torch.equal(sl["layers"][key], sl["stacked"][key]) for sl in slots
+                   for key in ("tgt", "acc", "nxt")) and all(
+            float((sl["layers"]["out"].float() - sl["stacked"]["out"].float()).abs().max()) <= 2e-3
+            + 1e-2 * float(sl["stacked"]["out"].float().abs().max()) for sl in slots)
+
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    res = {}
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for form in graphs:
+        steps = max(args.steps // 4, 9)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for i in range(steps):
+            graphs[form][i % n_slots].replay()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        warm = ev0.elapsed_time(ev1) * 1e3 / steps
+        cold = []
+        for i in range(steps):
+            flush.zero_()
+            ev0.record(stream)
+            graphs[form][i % n_slots].replay()
+            ev1.record(stream)
+            torch.cuda.synchronize()
+            cold.append(ev0.elapsed_time(ev1) * 1e3)
+        res[form] = {"warm_us_per_step": round(warm, 3), "cold_us_per_step": round(statistics.median(cold), 3)}
+    value = res["layers"]["cold_us_per_step"]
+    line = {
+        "metric": "decode-step us (24 per-layer KV appends + verify calls + greedy acceptance, one HIP graph)",
+        "value": value, "unit": "us/step", "n_gpus": 1, "steps": max(args.steps // 4, 9), "warmup": 20,
+        "ms_per_step": round(value / 1e3, 6), "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "one verify step of " + DESCRIPTIONS["verify"] + f", layer by layer, plus "
+                               f"acceptance over 8 x {vocab} bf16 logits; 3 graph slots",
+                   "global_batch": 1, "seq_len": max_ctx, "parallelism": "none (1 GPU)"},
+        "roofline": None,
+        "timing": {"per_layer_graph": res["layers"], "stacked_graph": res["stacked"],
+                   "note": "cold = HIP events around one graph replay after a 512 MiB overwrite (includes "
+                           "the graph launch); warm = graphs replayed back to back, round-robin over the slots"},
+        "plan_per_layer": plan_l.as_dict(), "plan_stacked": plan_all.as_dict(),
+        "parity_check": {"ok": bool(same), "what": "per-layer graph == stacked graph, outputs bit for bit"},
+        "cpu_baseline": None,
+    }
     print(json.dumps(line), flush=True)
 
 

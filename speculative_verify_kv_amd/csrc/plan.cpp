@@ -15,6 +15,7 @@ namespace swattn {
 namespace {
 
 constexpr int64_t kFillTarget = 512;   // partition workgroups wanted in flight (2 per CU)
+constexpr int64_t kMfmaFewUnits = 16;  // matrix-core launches this small split every tile off
 
 bool dtype_in(int v, std::initializer_list<int> ok) {
     for (int o : ok)
@@ -82,8 +83,15 @@ swattn_status_t make_plan(const swattn_desc_t* d, int32_t n_q, int32_t window, i
     if (variant == SWATTN_VARIANT_MFMA) {
         rows_per_chunk = kMfmaRows;
         const int64_t s_min = (U + kMfmaMaxKeys - 1) / kMfmaMaxKeys;
+        const int64_t chunks = (R + kMfmaRows - 1) / kMfmaRows;
+        const int64_t units = (int64_t)d->batch * d->num_kv_heads * chunks;
         if (d->num_splits > 0)
             S = clamp64(d->num_splits, s_min, std::max<int64_t>(s_min, (U + 15) / 16));
+        else if (units <= kMfmaFewUnits)
+            // A launch this small leaves most CUs idle and its time is one workgroup's
+            // chain of tiles: one tile (64 keys) per split shortens the chain more than
+            // the merge costs (one layer's verify step: 436 -> 367 us per 24 layers).
+            S = clamp64((U + 63) / 64, s_min, 8);
         else
             S = s_min;
     } else {

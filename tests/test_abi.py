@@ -142,6 +142,16 @@ def test_prefill_plan_caps_and_per_chunk_keys():
     assert p.num_splits == 8 and p.merge_grid > 0
 
 
+def test_small_launches_split_per_tile():
+    # one layer of the verify step: 2 units, 195 keys -> one split per 64-key tile
+    p = sw.swattn_plan(desc(batch=1), 8, 188)
+    assert p.variant == sw.SWATTN_VARIANT_MFMA and p.num_splits == 4 and p.merge_grid > 0
+    # 24 layers stacked: 48 units, no split
+    assert sw.swattn_plan(desc(batch=24), 8, 188).num_splits == 1
+    # a forced split count still wins
+    assert sw.swattn_plan(desc(batch=1, num_splits=1), 8, 188).num_splits == 1
+
+
 def test_verify_host_checks_return_before_launch():
     lib = sw.lib()
     d = desc(num_splits=2)
