@@ -49,10 +49,14 @@ typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef int int2_t __attribute__((ext_vector_type(2)));
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 
-constexpr int kT = 64;                     // keys per tile: 32 per key half
-
-template <int D, bool FP8>
+// KT = keys per tile.  64: two key halves of 32, one per wave pair, merged at the
+// end.  32: every wave takes all 32 keys of a tile and the waves split the output
+// columns instead, which halves the LDS a workgroup needs (no merge either).
+template <int D, bool FP8, int KT>
 struct Geo {
+    static constexpr int kT = KT;
+    static constexpr bool kSplitKeys = KT == 64;
+    static_assert(KT == 32 || KT == 64, "tiles of 32 or 64 keys");
     static constexpr int kElt = FP8 ? 1 : 2;
     static constexpr int kRowB = D * kElt;                  // bytes per cache row
     static constexpr int kCpr = kRowB / 16;                 // 16-byte chunks per row
@@ -70,8 +74,10 @@ struct Geo {
     // otherwise it has 4 waves.  Either way a SIMD runs two waves, so each may hold
     // 256 registers.
     static constexpr int kBlocks = 2 * (2 * kNS * kTileB + 14 * 1024) <= 160 * 1024 ? 2 : 1;
-    static constexpr int kND = kBlocks == 2 ? 1 : 2;        // column sets
-    static constexpr int kNW = 4 * kND;                     // waves: 2 row blocks x 2 key halves x kND
+    // column sets: 64-key tiles split them only where one workgroup fills the CU;
+    // 32-key tiles always split them in two (their waves do not split the keys)
+    static constexpr int kND = kSplitKeys ? (kBlocks == 2 ? 1 : 2) : 2;
+    static constexpr int kNW = kSplitKeys ? 4 * kND : 4;    // waves: row blocks x key halves x column sets
     static constexpr int kNT = kNW * 64;
     static constexpr int kShare = 2 * kNiK / kNW;           // load instructions per wave per tile
     static_assert(kShare * kNW == 2 * kNiK && kShare <= 16, "loads split evenly over the waves");
@@ -160,9 +166,10 @@ __device__ __forceinline__ void dma16(const void* src, const void* lds_dst) {
 }
 #pragma clang diagnostic pop
 
-template <int D, bool FP8, bool OUT_F32>
-__global__ __launch_bounds__((Geo<D, FP8>::kNT), (Geo<D, FP8>::kBlocks)) void partition_mfma_kernel(PartitionParams p) {
-    using G = Geo<D, FP8>;
+template <int D, bool FP8, bool OUT_F32, int KT>
+__global__ __launch_bounds__((Geo<D, FP8, KT>::kNT), (Geo<D, FP8, KT>::kBlocks)) void partition_mfma_kernel(PartitionParams p) {
+    using G = Geo<D, FP8, KT>;
+    constexpr int kT = KT;
     constexpr int NT = G::kNT;
     constexpr int KS = D / 32;                   // 32-dim k-steps of S^T = K Q^T
     constexpr int DH = D / G::kND;               // output columns of one wave set
@@ -189,8 +196,9 @@ __global__ __launch_bounds__((Geo<D, FP8>::kNT), (Geo<D, FP8>::kBlocks)) void pa
     const int l16 = lane & 15;
     const int q4 = lane >> 4;
     const int rb = wave & 1;                     // 16-row block
-    const int kh = (wave >> 1) & 1;              // key half of every tile
-    const int dh = wave >> 2;                    // column set (0 with 4 waves)
+    // key half of every tile (64-key tiles) and column set
+    const int kh = G::kSplitKeys ? (wave >> 1) & 1 : 0;
+    const int dh = G::kSplitKeys ? wave >> 2 : (wave >> 1) & 1;
 
     // grid (B * Hkv, row chunks, splits)
     const int s = blockIdx.z;
@@ -319,7 +327,7 @@ __global__ __launch_bounds__((Geo<D, FP8>::kNT), (Geo<D, FP8>::kBlocks)) void pa
     const int dcol0 = dh * DH;
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[db] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    const int kbase_t = kh * 32;             // this wave's keys within a tile
+    const int kbase_t = kh * 32;             // this wave's keys within a tile (32 of them)
 
     for (int t = 0; t < ntiles; ++t) {
         // This wave's loads of tile t have landed once only those of younger tiles are
@@ -512,6 +520,35 @@ __global__ __launch_bounds__((Geo<D, FP8>::kNT), (Geo<D, FP8>::kBlocks)) void pa
         }
     }
 
+    if constexpr (!G::kSplitKeys) {
+        // ---- every wave holds all keys of its rows: normalise and write its columns
+        if (qrow >= p.R) return;
+        const float poison = seq_ok ? 0.0f : __builtin_nanf("");
+        const float inv = l_run == 0.0f ? 0.0f : out_scale / l_run;   // a NaN sum must propagate
+        const int h = g * p.G + (qrow - qi * p.G);
+        const int64_t obase = (((int64_t)b * p.n_q + qi) * p.H + h) * D + dcol0 + q4 * 4;
+        const int64_t prow = (((int64_t)b * p.Hkv + g) * p.S + s) * p.R + qrow;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            const f32x4_t v = o[db] * inv + poison;
+            if (p.S == 1) {
+                if constexpr (OUT_F32) {
+                    *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(p.out) + obase + db * 16) = v;
+                } else {
+                    uint2 wq;
+                    wq.x = pack_bf16x2(v[0], v[1]);
+                    wq.y = pack_bf16x2(v[2], v[3]);
+                    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + obase + db * 16) = wq;
+                }
+            } else {
+                *reinterpret_cast<f32x4_t*>(p.ws_o + prow * D + dcol0 + db * 16 + q4 * 4) = v;
+            }
+        }
+        if (p.S > 1 && dh == 0 && q4 == 0)
+            p.ws_lse[prow] = (l_run == 0.0f ? -INFINITY : m_run + log2f(l_run)) + poison;
+        return;
+    }
+
     // ---- merge the two key halves of each row block, then write ---------------------
     // Wave (rb, kh, dh) keeps columns dcol0 + [kh*DH/2, kh*DH/2 + DH/2) and hands the
     // other half of its O^T, with its (max, sum), to its partner (rb, 1 - kh, dh).
@@ -569,22 +606,29 @@ __global__ __launch_bounds__((Geo<D, FP8>::kNT), (Geo<D, FP8>::kBlocks)) void pa
 
 
 
-template <int D>
-int launch_d(const PartitionParams& p, int grid, hipStream_t st) {
+template <int D, int KT>
+int launch_dk(const PartitionParams& p, int grid, hipStream_t st) {
     const bool fp8 = p.kv_dtype == SWATTN_FP8_E4M3;
     const bool of32 = p.out_dtype == SWATTN_F32;
     const dim3 grd((unsigned)(p.B * p.Hkv), (unsigned)p.row_chunks, (unsigned)p.S);
     if ((int64_t)grd.x * grd.y * grd.z != grid) return (int)hipErrorInvalidValue;
-    const dim3 blk(fp8 ? Geo<D, true>::kNT : Geo<D, false>::kNT);
+    const dim3 blk(fp8 ? Geo<D, true, KT>::kNT : Geo<D, false, KT>::kNT);
     if (fp8 && of32)
-        hipLaunchKernelGGL((partition_mfma_kernel<D, true, true>), grd, blk, 0, st, p);
+        hipLaunchKernelGGL((partition_mfma_kernel<D, true, true, KT>), grd, blk, 0, st, p);
     else if (fp8)
-        hipLaunchKernelGGL((partition_mfma_kernel<D, true, false>), grd, blk, 0, st, p);
+        hipLaunchKernelGGL((partition_mfma_kernel<D, true, false, KT>), grd, blk, 0, st, p);
     else if (of32)
-        hipLaunchKernelGGL((partition_mfma_kernel<D, false, true>), grd, blk, 0, st, p);
+        hipLaunchKernelGGL((partition_mfma_kernel<D, false, true, KT>), grd, blk, 0, st, p);
     else
-        hipLaunchKernelGGL((partition_mfma_kernel<D, false, false>), grd, blk, 0, st, p);
+        hipLaunchKernelGGL((partition_mfma_kernel<D, false, false, KT>), grd, blk, 0, st, p);
     return (int)hipGetLastError();
+}
+
+template <int D>
+int launch_d(const PartitionParams& p, int grid, hipStream_t st) {
+    if (p.tile_keys == 32) return launch_dk<D, 32>(p, grid, st);
+    if (p.tile_keys == 64) return launch_dk<D, 64>(p, grid, st);
+    return (int)hipErrorInvalidValue;
 }
 
 }  // namespace

@@ -13,6 +13,7 @@ constexpr int kWaveSize = 64;
 constexpr int kBlockThreads = 256;           // 4 waves: VALU partition and merge kernels
 constexpr int kMfmaRows = 32;                // query rows per matrix-core workgroup (two 16-row tiles)
 constexpr int kMfmaMaxKeys = 512;            // keys per matrix-core workgroup (cache-row table in LDS)
+constexpr int kComputeUnits = 256;           // MI355X
 constexpr int kValuRowsPerChunk = 8;         // query rows per VALU workgroup
 constexpr int kValuMaxKeys = 256;            // keys per VALU workgroup (score buffer size)
 constexpr int kValuKeyRound = 64;            // keys scored per round in the VALU kernel
@@ -35,6 +36,7 @@ struct PartitionParams {
     int32_t S, rows_per_chunk, row_chunks;
     int32_t q_dtype, kv_dtype, out_dtype;
     float scale_log2;     // scale * log2(e)
+    int32_t tile_keys;    // matrix-core kernel: keys per tile, 32 or 64
 };
 
 struct MergeParams {

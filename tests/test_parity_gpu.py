@@ -37,7 +37,8 @@ def test_named_workload(key):
     gu.check(got, ref, w.kv_dtype, out_f32=(w.q_dtype == "f32"), label=key)
 
 
-@pytest.mark.parametrize("key", ["verify", "wide_verify", "batched_fp8", "fullctx_2048", "prefill_512"])
+@pytest.mark.parametrize("key", ["verify", "wide_verify", "batched_fp8", "batched_bf16", "fullctx_2048",
+                                 "prefill_512"])
 def test_named_workload_f32_out(key):
     gu.log(f"[named f32 out] {key}")
     w, ref = gu.named(key)
@@ -208,6 +209,26 @@ def test_edge_shapes():
         got, plan = gu.run(w, out_f32=True)
         gu.log(f"  plan {plan.as_dict()}")
         gu.check(got, ref, w.kv_dtype, True, label=f"edge{k}")
+
+
+# ---------------------------------------------------------------------------
+# launches with more units than CUs take 32-key tiles (bfloat16, head_dim 256)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("S", [1, 2, 3])
+def test_many_units_32_key_tiles(S):
+    w = synth.make_workload("many", B=160, H=8, Hkv=2, D=256, n_q=8, window=188, ctx=None, bs=16, seed=21,
+                            recent=195, ctx_range=(8, 1200), max_blocks=80)
+    ref = gu.reference(w)
+    t = gu.upload(w)
+    first = None
+    for out_f32 in (True, False):
+        got, plan = gu.run(w, t=t, out_f32=out_f32, num_splits=S)
+        assert plan.grid == 160 * 2 * S
+        gu.check(got, ref, w.kv_dtype, out_f32, label=f"many S={S} f32={out_f32}")
+        if out_f32:
+            first = got
+    again, _ = gu.run(w, t=t, out_f32=True, num_splits=S)
+    assert np.array_equal(first, again)
 
 
 # ---------------------------------------------------------------------------
