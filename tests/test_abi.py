@@ -152,6 +152,16 @@ def test_small_launches_split_per_tile():
     assert sw.swattn_plan(desc(batch=1, num_splits=1), 8, 188).num_splits == 1
 
 
+def test_long_ranges_split_while_cus_idle():
+    # 48 units, contexts of 1024 under a 4096 window: four splits of 256 keys
+    # (192 workgroups on 256 CUs)
+    assert sw.swattn_plan(desc(max_ctx_len=1024), 8, 4096).num_splits == 4
+    # 4096 keys: the LDS table bound (8 splits) already fills the CUs
+    assert sw.swattn_plan(desc(), 8, 4096).num_splits == 8
+    # the verify window stays whole
+    assert sw.swattn_plan(desc(), 8, 188).num_splits == 1
+
+
 def test_verify_host_checks_return_before_launch():
     lib = sw.lib()
     d = desc(num_splits=2)
