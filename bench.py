@@ -119,51 +119,76 @@ def cpu_baseline(w, budget_s):
             "sample": f"whole workload, {len(times)} run(s), median; float64 numpy, 1 BLAS thread"}
 
 
+class ColdFlush:
+    """Puts the caches in a cold, clean state before a timed call: 512 MiB written
+    (twice the 256 MiB Infinity Cache, so nothing of the call's inputs stays cached),
+    then one byte of every 64-byte line of another 512 MiB read, which evicts the
+    written lines and makes their write-back happen here rather than inside the
+    timed call.  write_only() is the first half alone."""
+
+    def __init__(self, torch, dev):
+        self.w = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        self.r = torch.ones(512 << 20, dtype=torch.uint8, device=dev)
+        self.sink = torch.empty((512 << 20) // 64, dtype=torch.uint8, device=dev)
+
+    def write_only(self):
+        self.w.zero_()
+
+    def __call__(self):
+        self.w.zero_()
+        self.sink.copy_(self.r.view(-1, 64)[:, 0])
+
+
 def time_calls(torch, dev, stream, launch, flush, steps, with_graph):
     """Per-call times of ``launch(stream_handle)`` (one library call):
 
-    cold_graph: ``steps`` calls captured in one HIP graph, each after an overwrite
-    of ``flush`` (512 MiB: twice the Infinity Cache), minus the same graph without
-    the calls, over ``steps`` (median of three replays); cold_eager: HIP events
-    around each eager call (adds dispatch latency); warm: back to back, and
-    replayed from a graph of 100 calls."""
-    def capture(with_calls):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            cs = torch.cuda.current_stream(dev).cuda_stream
-            for _ in range(steps):
-                flush.zero_()
-                if with_calls:
-                    launch(cs)
-        return g
+    cold_graph: ``steps`` calls captured in one HIP graph, each after ``flush()``
+    (see ColdFlush), minus the same graph without the calls, over ``steps`` (median
+    of three replays); cold_graph_dirty: the same with the write half of the flush
+    only, so that the write-back of 512 MiB of dirty lines overlaps the call;
+    cold_eager: HIP events around each eager call (adds dispatch latency); warm:
+    back to back, and replayed from a graph of 100 calls."""
+    def cold_per_call(pre):
+        def capture(with_calls):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                cs = torch.cuda.current_stream(dev).cuda_stream
+                for _ in range(steps):
+                    pre()
+                    if with_calls:
+                        launch(cs)
+            return g
 
-    g_pair, g_flush = capture(True), capture(False)
-    g_pair.replay()
-    g_flush.replay()
-    torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-    per_call = []
-    wall = 0.0
-    for _ in range(3):
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        ev[0].record(stream)
+        g_pair, g_flush = capture(True), capture(False)
         g_pair.replay()
-        ev[1].record(stream)
-        torch.cuda.synchronize()
-        wall += time.perf_counter() - t0
-        ev[2].record(stream)
         g_flush.replay()
-        ev[3].record(stream)
         torch.cuda.synchronize()
-        per_call.append((ev[0].elapsed_time(ev[1]) - ev[2].elapsed_time(ev[3])) * 1e3 / steps)
-    cold_graph = statistics.median(per_call)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        per_call = []
+        wall = 0.0
+        for _ in range(3):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            ev[0].record(stream)
+            g_pair.replay()
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            wall += time.perf_counter() - t0
+            ev[2].record(stream)
+            g_flush.replay()
+            ev[3].record(stream)
+            torch.cuda.synchronize()
+            per_call.append((ev[0].elapsed_time(ev[1]) - ev[2].elapsed_time(ev[3])) * 1e3 / steps)
+        return statistics.median(per_call), per_call, wall
+
+    cold_graph, per_call, wall = cold_per_call(flush)
+    cold_dirty, _, _ = cold_per_call(flush.write_only)
 
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     torch.cuda.synchronize()
     for i in range(steps):
-        flush.zero_()
+        flush()
         starts[i].record(stream)
         launch(stream.cuda_stream)
         ends[i].record(stream)
@@ -197,15 +222,17 @@ def time_calls(torch, dev, stream, launch, flush, steps, with_graph):
     return {
         "cold_graph_us_per_call": round(cold_graph, 3),
         "cold_graph_samples_us": [round(x, 3) for x in per_call],
+        "cold_graph_dirty_us_per_call": round(cold_dirty, 3),
         "cold_eager_us_median": round(statistics.median(cold), 3),
         "cold_eager_us_p10": round(cold[int(0.1 * (len(cold) - 1))], 3),
         "cold_eager_us_p90": round(cold[int(0.9 * (len(cold) - 1))], 3),
         "warm_us_back_to_back": round(warm, 3),
         "graph_us_per_call_warm": None if graph_us is None else round(graph_us, 3),
         "timed_region_wall_s": round(wall, 4),
-        "note": "value = cold_graph: K calls in one HIP graph, each after a 512 MiB overwrite, "
-                "minus the same graph without the calls, over K; cold_eager = HIP events around "
-                "each eager call (adds dispatch latency)",
+        "note": "value = cold_graph: K calls in one HIP graph, each after a 512 MiB overwrite and "
+                "a 512 MiB read (inputs in HBM only, no dirty lines pending), minus the same graph "
+                "without the calls, over K; cold_graph_dirty: the overwrite alone; cold_eager = HIP "
+                "events around each eager call (adds dispatch latency)",
     }
 
 
@@ -289,9 +316,9 @@ def main():
     def launch(cs):
         call_lib(desc, q, k, v, bt, ctx, w.n_q, w.window, w.scale, out, ws, plan.workspace_bytes, cs)
 
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    flush = ColdFlush(torch, dev)
     for _ in range(args.warmup):
-        flush.zero_()
+        flush()
         launch(stream.cuda_stream)
     torch.cuda.synchronize()
 
@@ -385,7 +412,7 @@ def run_append(args, torch, np, sw, synth, dev):
     def launch(cs):
         sw.swattn_append_kv(d, kn_d, vn_d, sw.SWATTN_BF16, bt, ctx, n, k, v, cs)
 
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    flush = ColdFlush(torch, dev)
     for _ in range(args.warmup):
         launch(stream.cuda_stream)
     torch.cuda.synchronize()
@@ -457,7 +484,7 @@ def run_accept(args, torch, np, sw, dev):
     def launch(cs):
         sw.swattn_greedy_accept(logits, sw.SWATTN_BF16, B, n_q, vocab, d, tgt, acc, nxt, ws, ws.numel() * 8, cs)
 
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    flush = ColdFlush(torch, dev)
     for _ in range(args.warmup):
         launch(stream.cuda_stream)
     torch.cuda.synchronize()
@@ -579,7 +606,7 @@ def run_layer_graph(args, torch, np, sw, synth, dev):
             float((sl["layers"]["out"].float() - sl["stacked"]["out"].float()).abs().max()) <= 2e-3
             + 1e-2 * float(sl["stacked"]["out"].float().abs().max()) for sl in slots)
 
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    flush = ColdFlush(torch, dev)
     res = {}
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     for form in graphs:
@@ -593,7 +620,7 @@ def run_layer_graph(args, torch, np, sw, synth, dev):
         warm = ev0.elapsed_time(ev1) * 1e3 / steps
         cold = []
         for i in range(steps):
-            flush.zero_()
+            flush()
             ev0.record(stream)
             graphs[form][i % n_slots].replay()
             ev1.record(stream)
@@ -611,7 +638,7 @@ def run_layer_graph(args, torch, np, sw, synth, dev):
                    "global_batch": 1, "seq_len": max_ctx, "parallelism": "none (1 GPU)"},
         "roofline": None,
         "timing": {"per_layer_graph": res["layers"], "stacked_graph": res["stacked"],
-                   "note": "cold = HIP events around one graph replay after a 512 MiB overwrite (includes "
+                   "note": "cold = HIP events around one graph replay after a 512 MiB overwrite and read (includes "
                            "the graph launch); warm = graphs replayed back to back, round-robin over the slots"},
         "plan_per_layer": plan_l.as_dict(), "plan_stacked": plan_all.as_dict(),
         "parity_check": {"ok": bool(same), "what": "per-layer graph == stacked graph, outputs bit for bit"},

@@ -606,18 +606,25 @@ __global__ __launch_bounds__((Geo<D, FP8, KT>::kNT), (Geo<D, FP8, KT>::kBlocks))
 
 
 
-template <int D, int KT>
+template <int D, int KT, bool WITH_FP8>
 int launch_dk(const PartitionParams& p, int grid, hipStream_t st) {
     const bool fp8 = p.kv_dtype == SWATTN_FP8_E4M3;
     const bool of32 = p.out_dtype == SWATTN_F32;
     const dim3 grd((unsigned)(p.B * p.Hkv), (unsigned)p.row_chunks, (unsigned)p.S);
     if ((int64_t)grd.x * grd.y * grd.z != grid) return (int)hipErrorInvalidValue;
-    const dim3 blk(fp8 ? Geo<D, true, KT>::kNT : Geo<D, false, KT>::kNT);
-    if (fp8 && of32)
-        hipLaunchKernelGGL((partition_mfma_kernel<D, true, true, KT>), grd, blk, 0, st, p);
-    else if (fp8)
-        hipLaunchKernelGGL((partition_mfma_kernel<D, true, false, KT>), grd, blk, 0, st, p);
-    else if (of32)
+    if constexpr (WITH_FP8) {
+        if (fp8) {
+            const dim3 blk(Geo<D, true, KT>::kNT);
+            if (of32)
+                hipLaunchKernelGGL((partition_mfma_kernel<D, true, true, KT>), grd, blk, 0, st, p);
+            else
+                hipLaunchKernelGGL((partition_mfma_kernel<D, true, false, KT>), grd, blk, 0, st, p);
+            return (int)hipGetLastError();
+        }
+    }
+    if (fp8) return (int)hipErrorInvalidValue;
+    const dim3 blk(Geo<D, false, KT>::kNT);
+    if (of32)
         hipLaunchKernelGGL((partition_mfma_kernel<D, false, true, KT>), grd, blk, 0, st, p);
     else
         hipLaunchKernelGGL((partition_mfma_kernel<D, false, false, KT>), grd, blk, 0, st, p);
@@ -626,8 +633,12 @@ int launch_dk(const PartitionParams& p, int grid, hipStream_t st) {
 
 template <int D>
 int launch_d(const PartitionParams& p, int grid, hipStream_t st) {
-    if (p.tile_keys == 32) return launch_dk<D, 32>(p, grid, st);
-    if (p.tile_keys == 64) return launch_dk<D, 64>(p, grid, st);
+    // 32-key tiles exist for the one case where a 64-key workgroup fills a CU's LDS:
+    // bfloat16 caches with head_dim 256
+    if constexpr (D == 256) {
+        if (p.tile_keys == 32 && p.kv_dtype == SWATTN_BF16) return launch_dk<D, 32, false>(p, grid, st);
+    }
+    if (p.tile_keys == 64) return launch_dk<D, 64, true>(p, grid, st);
     return (int)hipErrorInvalidValue;
 }
 
