@@ -310,7 +310,7 @@ def main():
     plan = (sw.swattn_prefill_plan if prefill else sw.swattn_plan)(desc, w.n_q, w.window)
     call_lib = sw.swattn_prefill if prefill else sw.swattn_verify
     out = torch.empty(q.shape, dtype=torch.float32 if w.q_dtype == "f32" else torch.bfloat16, device=dev)
-    ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(plan.workspace_bytes, 256), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def launch(cs):
@@ -327,7 +327,7 @@ def main():
     got = out.float().cpu().numpy()
     rng = np.random.default_rng(0)
     worst = 0.0
-    for b in rng.choice(w.B, size=3, replace=False):
+    for b in rng.choice(w.B, size=min(3, w.B), replace=False):
         sub = dict(q=w.q[b:b + 1], block_table=w.block_table[b:b + 1], ctx_len=w.ctx_len[b:b + 1])
         ref = oracle.attend(sub["q"], w.k_cache, w.v_cache, sub["block_table"], sub["ctx_len"], w.n_q,
                             w.window, w.scale, q_format=w.q_format, kv_format=w.kv_format,
@@ -567,7 +567,7 @@ def run_layer_graph(args, torch, np, sw, synth, dev):
     plan_all = sw.swattn_plan(desc_all, n, w.window)
     assert plan_all.workspace_bytes == 0
     # the per-layer calls run one after another on the stream: one workspace serves them all
-    ws_l = torch.empty(max(plan_l.workspace_bytes, 256), dtype=torch.uint8, device=dev)
+    ws_l = torch.zeros(max(plan_l.workspace_bytes, 256), dtype=torch.uint8, device=dev)
 
     def step(slot, form, cs):
         o = slot[form]

@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define SWATTN_ABI_VERSION 1
+#define SWATTN_ABI_VERSION 2
 #define SWATTN_MAX_NQ 64          /* SPLITKV_VERIFY_MAX_Q of the manifest */
 #define SWATTN_MAX_PREFILL_NQ 512 /* MAX_NUM_BATCHED_TOKENS of the manifest */
 
@@ -73,6 +73,16 @@ typedef enum {
     SWATTN_VARIANT_MFMA = 2       /* bf16 matrix-core partition kernel (bf16 q, bf16/e4m3 kv) */
 } swattn_variant_t;
 
+/* How the partials of a split launch (S > 1) are combined. */
+typedef enum {
+    SWATTN_MERGE_AUTO = 0,        /* fused for up to 4 splits when the launch has few enough
+                                     row chunks, else the merge kernel */
+    SWATTN_MERGE_KERNEL = 1,      /* a separate merge kernel after the partition kernel */
+    SWATTN_MERGE_FUSED = 2        /* the last partition workgroup of each row chunk combines;
+                                     SWATTN_ERR_SHAPE when the launch has more row chunks
+                                     (B * Hkv * row_chunks) than counters */
+} swattn_merge_t;
+
 /* Problem description.  Plain data; the caller owns it. */
 typedef struct {
     int32_t batch;                /* B >= 1 independent problems */
@@ -90,6 +100,7 @@ typedef struct {
     const float* v_scale;         /* [Hkv] device fp32, same rule; stored value * scale = real value */
     int32_t num_splits;           /* 0: library chooses; > 0 forces the KV split count */
     int32_t variant;              /* swattn_variant_t; AUTO lets the library choose */
+    int32_t merge;                /* swattn_merge_t: how split partials are combined */
 } swattn_desc_t;
 
 /* What swattn_verify will launch for a description (filled by swattn_plan). */
@@ -99,9 +110,17 @@ typedef struct {
     int32_t rows_per_chunk;       /* query rows (n_q * H/Hkv packed) per workgroup */
     int32_t row_chunks;           /* row chunks per (problem, KV head) */
     int32_t grid;                 /* workgroups of the partition kernel */
-    int32_t merge_grid;           /* workgroups of the merge kernel (0 when S == 1) */
+    int32_t merge_grid;           /* workgroups of the merge kernel (0 when S == 1 or fused) */
+    int32_t fused_merge;          /* 1: the last partition workgroup of each row chunk to
+                                     finish combines the S partials itself (no merge kernel) */
     size_t workspace_bytes;       /* device scratch swattn_verify needs (0 when S == 1) */
 } swattn_plan_t;
+
+/* A split plan's workspace starts with this many bytes of arrival counters, the
+ * same region for every plan.  They must be zero before the first call that uses
+ * the workspace (swattn_workspace_init, or any zero fill); every call leaves them
+ * zero, so one fill serves all later calls, with any plan. */
+#define SWATTN_WORKSPACE_COUNTER_BYTES 4096
 
 /*
  * swattn_plan — validate a description and choose the launch.  Pure host code:
@@ -110,6 +129,11 @@ typedef struct {
  */
 swattn_status_t swattn_plan(const swattn_desc_t* desc, int32_t n_q, int32_t window,
                             swattn_plan_t* plan);
+
+/* Zero the arrival counters of a fresh workspace of `bytes` bytes (16-byte aligned,
+ * device memory) on `stream`: one small kernel, no memset, so it may be captured in
+ * a graph.  Needed once per workspace; a zero-filled allocation needs nothing. */
+swattn_status_t swattn_workspace_init(void* workspace, size_t bytes, void* stream);
 
 /* Convenience: workspace size in bytes for (desc, n_q, window); pure host code. */
 swattn_status_t swattn_workspace_bytes(const swattn_desc_t* desc, int32_t n_q, int32_t window,
@@ -130,8 +154,10 @@ swattn_status_t swattn_workspace_bytes(const swattn_desc_t* desc, int32_t n_q, i
  *   scale       finite softmax scale (usually 1/sqrt(D))
  *   out         [B][n_q][H][D] out_dtype, device; fully overwritten; must not alias q
  *   workspace   device scratch of >= plan.workspace_bytes (may be NULL when that is 0);
- *               contents are undefined afterwards; calls that overlap in time need
- *               separate workspaces
+ *               its first SWATTN_WORKSPACE_COUNTER_BYTES must be zero on entry (see
+ *               swattn_workspace_init) and are zero again on completion; the rest is
+ *               undefined afterwards; calls that overlap in time need separate
+ *               workspaces
  *   stream      hipStream_t (NULL = default stream)
  *
  * All data pointers must be 16-byte aligned.  Host-checkable errors are returned

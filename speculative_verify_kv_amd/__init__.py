@@ -3,7 +3,7 @@
 Argument marshalling only: every step of the computation runs in the HIP
 kernels of ``libswattn.so``.  The functions mirror the C ABI in
 ``include/swattn.h`` one for one (``swattn_plan``, ``swattn_workspace_bytes``,
-``swattn_verify``, ``swattn_prefill_plan``, ``swattn_prefill``,
+``swattn_workspace_init``, ``swattn_verify``, ``swattn_prefill_plan``, ``swattn_prefill``,
 ``swattn_append_kv``, ``swattn_greedy_accept_workspace``,
 ``swattn_greedy_accept``, ``swattn_check_inputs``, ``swattn_status_str``,
 ``swattn_abi_version``);
@@ -19,6 +19,8 @@ LIB_PATH = os.path.join(_HERE, "libswattn.so")
 
 SWATTN_F32, SWATTN_BF16, SWATTN_FP8_E4M3 = 0, 1, 2
 SWATTN_VARIANT_AUTO, SWATTN_VARIANT_VALU, SWATTN_VARIANT_MFMA = 0, 1, 2
+SWATTN_MERGE_AUTO, SWATTN_MERGE_KERNEL, SWATTN_MERGE_FUSED = 0, 1, 2
+SWATTN_WORKSPACE_COUNTER_BYTES = 4096
 SWATTN_MAX_NQ = 64
 SWATTN_MAX_PREFILL_NQ = 512
 
@@ -30,7 +32,7 @@ STATUS = {
 }
 
 # Symbols declared in include/swattn.h.
-EXPORTED = ("swattn_plan", "swattn_workspace_bytes", "swattn_verify", "swattn_prefill_plan",
+EXPORTED = ("swattn_plan", "swattn_workspace_bytes", "swattn_workspace_init", "swattn_verify", "swattn_prefill_plan",
             "swattn_prefill", "swattn_append_kv", "swattn_greedy_accept_workspace",
             "swattn_greedy_accept", "swattn_check_inputs", "swattn_status_str", "swattn_abi_version")
 
@@ -50,7 +52,7 @@ class swattn_desc_t(ctypes.Structure):
         ("num_blocks", ctypes.c_int32), ("max_ctx_len", ctypes.c_int32),
         ("q_dtype", ctypes.c_int), ("kv_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int),
         ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
-        ("num_splits", ctypes.c_int32), ("variant", ctypes.c_int32),
+        ("num_splits", ctypes.c_int32), ("variant", ctypes.c_int32), ("merge", ctypes.c_int32),
     ]
 
 
@@ -58,7 +60,7 @@ class swattn_plan_t(ctypes.Structure):
     _fields_ = [
         ("variant", ctypes.c_int32), ("num_splits", ctypes.c_int32),
         ("rows_per_chunk", ctypes.c_int32), ("row_chunks", ctypes.c_int32),
-        ("grid", ctypes.c_int32), ("merge_grid", ctypes.c_int32),
+        ("grid", ctypes.c_int32), ("merge_grid", ctypes.c_int32), ("fused_merge", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_size_t),
     ]
 
@@ -67,7 +69,7 @@ class swattn_plan_t(ctypes.Structure):
 
 
 _lib = None
-ABI_VERSION = 1          # SWATTN_ABI_VERSION these ctypes mirrors follow
+ABI_VERSION = 2          # SWATTN_ABI_VERSION these ctypes mirrors follow
 
 
 def lib():
@@ -88,6 +90,8 @@ def lib():
         L.swattn_workspace_bytes.argtypes = [P(swattn_desc_t), ctypes.c_int32, ctypes.c_int32,
                                              P(ctypes.c_size_t)]
         L.swattn_workspace_bytes.restype = ctypes.c_int
+        L.swattn_workspace_init.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        L.swattn_workspace_init.restype = ctypes.c_int
         L.swattn_verify.argtypes = [P(swattn_desc_t), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
                                     ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
@@ -150,6 +154,12 @@ def swattn_prefill_plan(desc, n_q, window, check=True):
     if check and st != 0:
         raise SwattnError(st, "swattn_prefill_plan")
     return plan if check else (st, plan)
+
+
+def swattn_workspace_init(workspace, nbytes, stream=None):
+    st = lib().swattn_workspace_init(_ptr(workspace), int(nbytes), _ptr(stream))
+    if st != 0:
+        raise SwattnError(st, "swattn_workspace_init")
 
 
 def swattn_workspace_bytes(desc, n_q, window):
@@ -246,7 +256,7 @@ def _dtype_code(t):
 
 
 def make_desc(q, k_cache, block_table, max_ctx_len, out_dtype=None, k_scale=None, v_scale=None,
-              num_splits=0, variant=SWATTN_VARIANT_AUTO):
+              num_splits=0, variant=SWATTN_VARIANT_AUTO, merge=SWATTN_MERGE_AUTO):
     """Descriptor for q [B, n_q, H, D], k_cache [num_blocks, Hkv, bs, D],
     block_table [B, max_blocks]; out_dtype defaults to q's dtype."""
     B, _, H, D = q.shape
@@ -262,25 +272,27 @@ def make_desc(q, k_cache, block_table, max_ctx_len, out_dtype=None, k_scale=None
     d.v_scale = _ptr(v_scale)
     d.num_splits = int(num_splits)
     d.variant = int(variant)
+    d.merge = int(merge)
     return d
 
 
 def verify(q, k_cache, v_cache, block_table, ctx_len, n_q, window, scale, max_ctx_len,
            out=None, out_dtype=None, k_scale=None, v_scale=None, num_splits=0,
-           variant=SWATTN_VARIANT_AUTO, workspace=None, stream=None, prefill=False):
+           variant=SWATTN_VARIANT_AUTO, workspace=None, stream=None, prefill=False,
+           merge=SWATTN_MERGE_AUTO):
     """Run swattn_verify (or swattn_prefill) on torch device tensors; returns (out, plan).
 
-    Allocates ``out`` and the workspace with torch when they are not given (a
-    caller under graph capture passes both)."""
+    Allocates ``out`` and a zero-filled workspace with torch when they are not given
+    (a caller under graph capture passes both)."""
     import torch
     desc = make_desc(q, k_cache, block_table, max_ctx_len, out_dtype, k_scale, v_scale,
-                     num_splits, variant)
+                     num_splits, variant, merge)
     plan = (swattn_prefill_plan if prefill else swattn_plan)(desc, n_q, window)
     if out is None:
         tdt = torch.float32 if desc.out_dtype == SWATTN_F32 else torch.bfloat16
         out = torch.empty(q.shape, dtype=tdt, device=q.device)
     if workspace is None and plan.workspace_bytes > 0:
-        workspace = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(plan.workspace_bytes, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream

@@ -54,13 +54,16 @@ swattn_status_t attend(const swattn_desc_t* d, const void* q, const void* k_cach
     }
     float* ws_o = nullptr;
     float* ws_lse = nullptr;
+    int32_t* counters = nullptr;
     if (plan.workspace_bytes > 0) {
         if (!workspace || workspace_bytes < plan.workspace_bytes) return SWATTN_ERR_WORKSPACE;
         if (!aligned(workspace, 16)) return SWATTN_ERR_ALIGN;
         const int64_t rows_total = (int64_t)d->batch * d->num_kv_heads * R;
         const int64_t o_bytes = ((rows_total * plan.num_splits * d->head_dim * 4) + 255) / 256 * 256;
-        ws_o = reinterpret_cast<float*>(workspace);
-        ws_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + o_bytes);
+        char* base = reinterpret_cast<char*>(workspace);
+        if (plan.fused_merge) counters = reinterpret_cast<int32_t*>(base);
+        ws_o = reinterpret_cast<float*>(base + SWATTN_WORKSPACE_COUNTER_BYTES);
+        ws_lse = reinterpret_cast<float*>(base + SWATTN_WORKSPACE_COUNTER_BYTES + o_bytes);
     }
 
     PartitionParams p;
@@ -74,6 +77,7 @@ swattn_status_t attend(const swattn_desc_t* d, const void* q, const void* k_cach
     p.out = out;
     p.ws_o = ws_o;
     p.ws_lse = ws_lse;
+    p.counters = counters;
     p.B = d->batch;
     p.H = d->num_heads;
     p.Hkv = d->num_kv_heads;
@@ -244,6 +248,14 @@ swattn_status_t accept_shape(int32_t batch, int32_t n_q, int32_t vocab, int64_t*
 
 }  // namespace
 }  // namespace swattn
+
+extern "C" swattn_status_t swattn_workspace_init(void* workspace, size_t bytes, void* stream) {
+    if (!workspace) return SWATTN_ERR_NULL;
+    if (!swattn::aligned(workspace, 16)) return SWATTN_ERR_ALIGN;
+    const size_t n = (bytes < SWATTN_WORKSPACE_COUNTER_BYTES ? bytes : SWATTN_WORKSPACE_COUNTER_BYTES) / 4;
+    return swattn::launch_zero_words(reinterpret_cast<int32_t*>(workspace), (int)n, stream) == 0 ? SWATTN_OK
+                                                                                                : SWATTN_ERR_HIP;
+}
 
 extern "C" swattn_status_t swattn_greedy_accept_workspace(int32_t batch, int32_t n_q, int32_t vocab,
                                                           size_t* bytes) {

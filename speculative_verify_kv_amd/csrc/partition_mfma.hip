@@ -40,6 +40,7 @@
 #include <hip/hip_runtime.h>
 
 #include "kv_access.h"
+#include "split_merge.h"
 #include "swattn_internal.h"
 
 namespace swattn {
@@ -522,7 +523,7 @@ __global__ __launch_bounds__((Geo<D, FP8, KT>::kNT), (Geo<D, FP8, KT>::kBlocks))
 
     if constexpr (!G::kSplitKeys) {
         // ---- every wave holds all keys of its rows: normalise and write its columns
-        if (qrow >= p.R) return;
+        if (qrow < p.R) {
         const float poison = seq_ok ? 0.0f : __builtin_nanf("");
         const float inv = l_run == 0.0f ? 0.0f : out_scale / l_run;   // a NaN sum must propagate
         const int h = g * p.G + (qrow - qi * p.G);
@@ -541,13 +542,13 @@ __global__ __launch_bounds__((Geo<D, FP8, KT>::kNT), (Geo<D, FP8, KT>::kBlocks))
                     *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + obase + db * 16) = wq;
                 }
             } else {
-                *reinterpret_cast<f32x4_t*>(p.ws_o + prow * D + dcol0 + db * 16 + q4 * 4) = v;
+                store_partial4(p, p.ws_o + prow * D + dcol0 + db * 16 + q4 * 4, v);
             }
         }
         if (p.S > 1 && dh == 0 && q4 == 0)
-            p.ws_lse[prow] = (l_run == 0.0f ? -INFINITY : m_run + log2f(l_run)) + poison;
-        return;
-    }
+            store_partial1(p, p.ws_lse + prow, (l_run == 0.0f ? -INFINITY : m_run + log2f(l_run)) + poison);
+        }
+    } else {
 
     // ---- merge the two key halves of each row block, then write ---------------------
     // Wave (rb, kh, dh) keeps columns dcol0 + [kh*DH/2, kh*DH/2 + DH/2) and hands the
@@ -577,7 +578,7 @@ __global__ __launch_bounds__((Geo<D, FP8, KT>::kNT), (Geo<D, FP8, KT>::kBlocks))
     const float* src = xo + (((rb * 2 + (1 - kh)) * G::kND + dh) * 16 + l16) * (DH / 2);
     const int mcol = dcol0 + kh * (DH / 2);                    // the columns this wave writes
 
-    if (qrow >= p.R) return;
+    if (qrow < p.R) {
     const float poison = seq_ok ? 0.0f : __builtin_nanf("");
     const float inv = l_all == 0.0f ? 0.0f : out_scale / l_all;   // a NaN sum must propagate
     const int h = g * p.G + (qrow - qi * p.G);
@@ -597,11 +598,16 @@ __global__ __launch_bounds__((Geo<D, FP8, KT>::kNT), (Geo<D, FP8, KT>::kBlocks))
                 *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + obase + db * 16) = wq;
             }
         } else {
-            *reinterpret_cast<f32x4_t*>(p.ws_o + prow * D + mcol + db * 16 + q4 * 4) = v;
+            store_partial4(p, p.ws_o + prow * D + mcol + db * 16 + q4 * 4, v);
         }
     }
     if (p.S > 1 && kh == 0 && dh == 0 && q4 == 0)
-        p.ws_lse[prow] = (l_all == 0.0f ? -INFINITY : m_all + log2f(l_all)) + poison;
+        store_partial1(p, p.ws_lse + prow, (l_all == 0.0f ? -INFINITY : m_all + log2f(l_all)) + poison);
+    }
+    }
+
+    // ---- split launches: the last workgroup of the row chunk combines the partials
+    if (p.counters != nullptr) merge_if_last<D, OUT_F32, NT>(p, b, g, rc);
 }
 
 

@@ -20,6 +20,7 @@
 #include <hip/hip_runtime.h>
 
 #include "kv_access.h"
+#include "split_merge.h"
 #include "swattn_internal.h"
 
 namespace swattn {
@@ -267,10 +268,17 @@ __global__ __launch_bounds__(kBlockThreads) void partition_valu_kernel(Partition
                 reinterpret_cast<uint16_t*>(p.out)[oi] = (uint16_t)f32_to_bf16_bits(val);
         } else {
             const int64_t prow = (((int64_t)b * p.Hkv + g) * p.S + s) * p.R + r;
-            p.ws_o[prow * D + d] = val;
+            store_partial1(p, p.ws_o + prow * D + d, val);
             if (d == 0)
-                p.ws_lse[prow] = (L == 0.0f ? -INFINITY : rstat[rr][0] + log2f(L)) + poison;
+                store_partial1(p, p.ws_lse + prow, (L == 0.0f ? -INFINITY : rstat[rr][0] + log2f(L)) + poison);
         }
+    }
+    // split launches: the last workgroup of the row chunk combines the partials
+    if (p.counters != nullptr) {
+        if (p.out_dtype == SWATTN_F32)
+            merge_if_last<D, true, kBlockThreads>(p, b, g, rc);
+        else
+            merge_if_last<D, false, kBlockThreads>(p, b, g, rc);
     }
 }
 

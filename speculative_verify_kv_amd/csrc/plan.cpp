@@ -16,6 +16,7 @@ namespace {
 
 constexpr int64_t kFillTarget = 512;   // partition workgroups wanted in flight (2 per CU)
 constexpr int64_t kMfmaFewUnits = 16;  // matrix-core launches this small split every tile off
+constexpr int64_t kFusedMaxSplits = 4;  // automatic fused merge up to this many splits
 
 bool dtype_in(int v, std::initializer_list<int> ok) {
     for (int o : ok)
@@ -52,6 +53,7 @@ swattn_status_t validate_desc(const swattn_desc_t* d, int32_t n_q, int32_t windo
     if (d->num_splits < 0) return SWATTN_ERR_ARG;
     if (!dtype_in(d->variant, {SWATTN_VARIANT_AUTO, SWATTN_VARIANT_VALU, SWATTN_VARIANT_MFMA}))
         return SWATTN_ERR_ARG;
+    if (!dtype_in(d->merge, {SWATTN_MERGE_AUTO, SWATTN_MERGE_KERNEL, SWATTN_MERGE_FUSED})) return SWATTN_ERR_ARG;
     if (d->variant == SWATTN_VARIANT_MFMA &&
         (d->q_dtype != SWATTN_BF16 || d->kv_dtype == SWATTN_F32))
         return SWATTN_ERR_DTYPE;
@@ -117,13 +119,25 @@ swattn_status_t make_plan(const swattn_desc_t* d, int32_t n_q, int32_t window, i
     const int64_t rows_total = (int64_t)d->batch * d->num_kv_heads * R;
     const int64_t merge_rows_per_wg = (kBlockThreads * 4) / D;   // D/4 threads per row
     int64_t merge_grid = 0;
+    int32_t fused = 0;
     size_t ws = 0;
     if (S > 1) {
-        // layout: [partial outputs][partial log2-sum-exps]
-        merge_grid = (rows_total + merge_rows_per_wg - 1) / merge_rows_per_wg;
-        if (merge_grid > INT32_MAX) return SWATTN_ERR_SHAPE;
+        // The last workgroup of each row chunk combines the partials (no second launch)
+        // when the chunks fit the counter region and there are at most kFusedMaxSplits
+        // partials per row; otherwise a merge kernel does.  Measured (MI355X, cold): one
+        // sequence of tiny decode at S = 3, 13.5 -> 12.6 us; full context 4096 at S = 8,
+        // 49 -> 54 us (one workgroup then reads 256 KiB of partials on its own).
+        const int64_t chunks_total = (int64_t)d->batch * d->num_kv_heads * row_chunks;
+        if (d->merge == SWATTN_MERGE_FUSED && chunks_total > kMergeCounters) return SWATTN_ERR_SHAPE;
+        fused = d->merge == SWATTN_MERGE_FUSED ||
+                (d->merge == SWATTN_MERGE_AUTO && chunks_total <= kMergeCounters && S <= kFusedMaxSplits);
+        if (!fused) {
+            merge_grid = (rows_total + merge_rows_per_wg - 1) / merge_rows_per_wg;
+            if (merge_grid > INT32_MAX) return SWATTN_ERR_SHAPE;
+        }
+        // layout: [arrival counters][partial outputs][partial log2-sum-exps]
         const int64_t o_bytes = ((rows_total * S * D * 4) + 255) / 256 * 256;
-        ws = (size_t)(o_bytes + rows_total * S * 4);
+        ws = (size_t)(SWATTN_WORKSPACE_COUNTER_BYTES + o_bytes + rows_total * S * 4);
     }
     out->variant = variant;
     out->num_splits = (int32_t)S;
@@ -131,6 +145,7 @@ swattn_status_t make_plan(const swattn_desc_t* d, int32_t n_q, int32_t window, i
     out->row_chunks = (int32_t)row_chunks;
     out->grid = (int32_t)grid;
     out->merge_grid = (int32_t)merge_grid;
+    out->fused_merge = fused;
     out->workspace_bytes = ws;
     return SWATTN_OK;
 }

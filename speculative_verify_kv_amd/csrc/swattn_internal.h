@@ -17,6 +17,11 @@ constexpr int kComputeUnits = 256;           // MI355X
 constexpr int kValuRowsPerChunk = 8;         // query rows per VALU workgroup
 constexpr int kValuMaxKeys = 256;            // keys per VALU workgroup (score buffer size)
 constexpr int kValuKeyRound = 64;            // keys scored per round in the VALU kernel
+// Split launches keep one arrival counter per (problem, KV head, row chunk) at the
+// start of the workspace, in a region of fixed size for every plan, so that no plan's
+// partials ever overwrite another plan's counters.  Launches with more units than
+// counters use the separate merge kernel instead.
+constexpr int kMergeCounters = SWATTN_WORKSPACE_COUNTER_BYTES / 4;
 
 // Everything a partition kernel needs, passed by value.
 struct PartitionParams {
@@ -30,6 +35,7 @@ struct PartitionParams {
     void* out;
     float* ws_o;          // [B*Hkv][S][R][D] normalised partial outputs (S > 1)
     float* ws_lse;        // [B*Hkv][S][R] log2-sum-exp of each partial (S > 1)
+    int32_t* counters;    // [B*Hkv][row_chunks] arrivals (fused merge), else NULL
     int32_t B, H, Hkv, G, D, bs, max_blocks, num_blocks;
     int32_t bs_log2;      // log2(bs) when bs is a power of two, else -1
     int32_t n_q, window, R, max_ctx;
@@ -81,6 +87,7 @@ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 int launch_partition_mfma(const PartitionParams& p, int grid, void* stream);
 int launch_partition_valu(const PartitionParams& p, int grid, void* stream);
 int launch_merge(const MergeParams& p, int grid, void* stream);
+int launch_zero_words(int32_t* w, int n, void* stream);
 int launch_kv_append(const AppendParams& p, int grid, void* stream);
 int launch_accept(const AcceptParams& p, int grid1, void* stream);
 

@@ -28,7 +28,7 @@ def test_library_exports_every_header_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert sw.swattn_abi_version() == sw.ABI_VERSION == 1
+    assert sw.swattn_abi_version() == sw.ABI_VERSION == 2
     for code in sw.STATUS:
         s = sw.swattn_status_str(code)
         assert s and s != "unknown status"
@@ -40,7 +40,7 @@ def desc(**kw):
     base = dict(batch=24, num_heads=8, num_kv_heads=2, head_dim=256, block_size=16,
                 max_blocks_per_seq=256, num_blocks=6144, max_ctx_len=4096,
                 q_dtype=sw.SWATTN_BF16, kv_dtype=sw.SWATTN_BF16, out_dtype=sw.SWATTN_BF16,
-                k_scale=None, v_scale=None, num_splits=0, variant=0)
+                k_scale=None, v_scale=None, num_splits=0, variant=0, merge=0)
     base.update(kw)
     for k, v in base.items():
         setattr(d, k, v)
@@ -73,6 +73,8 @@ def status(d, n_q=8, window=188):
     (dict(variant=sw.SWATTN_VARIANT_MFMA, kv_dtype=sw.SWATTN_F32), 8, 188, "SWATTN_ERR_DTYPE"),
     (dict(variant=9), 8, 188, "SWATTN_ERR_ARG"),
     (dict(num_splits=-1), 8, 188, "SWATTN_ERR_ARG"),
+    (dict(merge=3), 8, 188, "SWATTN_ERR_ARG"),
+    (dict(merge=-1), 8, 188, "SWATTN_ERR_ARG"),
     (dict(), 8, 188, "SWATTN_OK"),
     (dict(), 64, 188, "SWATTN_OK"),
     (dict(), 1, 2 ** 31 - 1, "SWATTN_OK"),
@@ -96,14 +98,25 @@ def test_plan_variants_and_workspace():
     assert p.variant == sw.SWATTN_VARIANT_MFMA and p.rows_per_chunk == 32 and p.row_chunks == 1
     assert p.grid == 24 * 2 * p.num_splits
     R, D, units = 32, 256, 24 * 2
-    # split plans: [partial outputs][partial log2-sum-exps] and a merge launch
+    # split plans: [counters][partial outputs][partial log2-sum-exps]; the partition
+    # kernel combines the partials itself, or a merge kernel does when asked to
     for S in (2, 5):
         for variant in (sw.SWATTN_VARIANT_MFMA, sw.SWATTN_VARIANT_VALU):
-            p = sw.swattn_plan(desc(num_splits=S, variant=variant), 8, 188)
-            o_bytes = -(-(units * R * S * D * 4) // 256) * 256
-            assert p.num_splits == S and p.variant == variant
-            assert p.workspace_bytes == o_bytes + units * R * S * 4
-            assert p.merge_grid == -(-(units * R) // (1024 // D))
+            for merge in (sw.SWATTN_MERGE_AUTO, sw.SWATTN_MERGE_FUSED, sw.SWATTN_MERGE_KERNEL):
+                p = sw.swattn_plan(desc(num_splits=S, variant=variant, merge=merge), 8, 188)
+                o_bytes = -(-(units * R * S * D * 4) // 256) * 256
+                assert p.num_splits == S and p.variant == variant
+                assert p.workspace_bytes == sw.SWATTN_WORKSPACE_COUNTER_BYTES + o_bytes + units * R * S * 4
+                if merge == sw.SWATTN_MERGE_KERNEL or (merge == sw.SWATTN_MERGE_AUTO and S > 4):
+                    assert p.fused_merge == 0 and p.merge_grid == -(-(units * R) // (1024 // D))
+                else:
+                    assert p.fused_merge == 1 and p.merge_grid == 0
+    # more row chunks than counters: a merge kernel, and a forced fused merge is refused
+    many = dict(batch=600, max_blocks_per_seq=16, max_ctx_len=256, num_splits=2)
+    p = sw.swattn_plan(desc(**many), 8, 188)
+    assert p.num_splits == 2 and p.fused_merge == 0 and p.merge_grid > 0
+    assert status(desc(merge=sw.SWATTN_MERGE_FUSED, **many)) == "SWATTN_ERR_SHAPE"
+    assert sw.swattn_plan(desc(merge=sw.SWATTN_MERGE_FUSED, **dict(many, batch=512)), 8, 188).fused_merge == 1
     assert sw.swattn_workspace_bytes(desc(), 8, 188) == sw.swattn_plan(desc(), 8, 188).workspace_bytes
     # decode: 4 rows -> vector ALU
     p = sw.swattn_plan(desc(), 1, 188)
@@ -116,7 +129,7 @@ def test_plan_variants_and_workspace():
     assert p.rows_per_chunk == 32 and p.row_chunks == 8
     # forced split count is honoured (within the chunk count), S = 1 needs no workspace
     p = sw.swattn_plan(desc(num_splits=1), 8, 188)
-    assert p.num_splits == 1 and p.workspace_bytes == 0 and p.merge_grid == 0
+    assert p.num_splits == 1 and p.workspace_bytes == 0 and p.merge_grid == 0 and p.fused_merge == 0
     p = sw.swattn_plan(desc(num_splits=3), 8, 188)
     assert p.num_splits == 3 and p.workspace_bytes > 0
     p = sw.swattn_plan(desc(num_splits=1000), 8, 188)
@@ -145,7 +158,7 @@ def test_prefill_plan_caps_and_per_chunk_keys():
 def test_small_launches_split_per_tile():
     # one layer of the verify step: 2 units, 195 keys -> one split per 64-key tile
     p = sw.swattn_plan(desc(batch=1), 8, 188)
-    assert p.variant == sw.SWATTN_VARIANT_MFMA and p.num_splits == 4 and p.merge_grid > 0
+    assert p.variant == sw.SWATTN_VARIANT_MFMA and p.num_splits == 4 and p.fused_merge == 1
     # 24 layers stacked: 48 units, no split
     assert sw.swattn_plan(desc(batch=24), 8, 188).num_splits == 1
     # a forced split count still wins

@@ -65,6 +65,42 @@ def test_split_invariance_and_determinism_mfma():
         assert np.abs(outs[S] - outs[1]).max() <= 2e-3
 
 
+@pytest.mark.parametrize("key,variant", [("verify", sw.SWATTN_VARIANT_MFMA), ("batched_fp8", sw.SWATTN_VARIANT_MFMA),
+                                         ("tiny_decode", sw.SWATTN_VARIANT_VALU), ("verify", sw.SWATTN_VARIANT_VALU)])
+def test_fused_merge_equals_merge_kernel(key, variant):
+    """The last partition workgroup of a row chunk combines the partials with the same
+    code as the merge kernel: identical outputs.  Calls alternate between two query
+    sets on one workspace, so a partial read before its writer's stores landed, or a
+    counter not reset, shows as a mismatch."""
+    w, ref = gu.named(key)
+    t = gu.upload(w)
+    q_sets = [t["q"], (-t["q"]).contiguous()]
+    S_list = (2, 3, 4, 8) if key != "batched_fp8" else (2,)
+    mc = int(w.ctx_len.max())
+    odt = sw.SWATTN_F32
+
+    def call(q, S, merge, ws):
+        out, plan = sw.verify(q, t["k"], t["v"], t["bt"], t["ctx"], w.n_q, w.window, w.scale, mc,
+                              out_dtype=odt, k_scale=t["ks"], v_scale=t["vs"], num_splits=S,
+                              variant=variant, merge=merge, workspace=ws)
+        torch.cuda.synchronize()
+        return out.cpu().numpy().astype(np.float64), plan
+
+    for S in S_list:
+        gu.log(f"[fused merge] {key} variant={variant} S={S}")
+        kern = [call(q, S, sw.SWATTN_MERGE_KERNEL, None) for q in q_sets]
+        assert kern[0][1].merge_grid > 0 and kern[0][1].fused_merge == 0
+        gu.check(kern[0][0], ref, w.kv_dtype, True, label=f"{key} S={S} merge kernel")
+        plan = kern[0][1]
+        ws = torch.zeros(plan.workspace_bytes, dtype=torch.uint8, device=gu.DEV)
+        for rep in range(6):
+            got, fplan = call(q_sets[rep % 2], S, sw.SWATTN_MERGE_FUSED, ws)
+            assert fplan.num_splits == S and fplan.variant == variant
+            assert fplan.fused_merge == 1 and fplan.merge_grid == 0
+            assert np.array_equal(got, kern[rep % 2][0]), f"{key} S={S} call {rep}: fused != merge kernel"
+        assert int(ws[:sw.SWATTN_WORKSPACE_COUNTER_BYTES].count_nonzero()) == 0
+
+
 def test_split_invariance_valu_decode():
     w = synth.make_workload("decode", B=6, H=8, Hkv=2, D=256, n_q=1, window=188, ctx=[300, 188, 1, 4096, 189, 2000],
                             bs=16, seed=5, recent=188, max_blocks=256)
@@ -308,17 +344,21 @@ def test_workspace_reuse_across_split_counts():
     t = gu.upload(w)
     big = sw.swattn_plan(sw.make_desc(t["q"], t["k"], t["bt"], 4096, num_splits=5), w.n_q, w.window)
     ws = torch.full((big.workspace_bytes,), 0x7F, dtype=torch.uint8, device=gu.DEV)   # stale bytes
+    sw.swattn_workspace_init(ws, ws.numel(), torch.cuda.current_stream().cuda_stream)   # counters only
     first = {}
-    for S in (2, 5, 3, 5, 2):
+    for S, merge in ((2, sw.SWATTN_MERGE_FUSED), (5, sw.SWATTN_MERGE_KERNEL), (3, sw.SWATTN_MERGE_FUSED),
+                     (5, sw.SWATTN_MERGE_FUSED), (2, sw.SWATTN_MERGE_KERNEL), (2, sw.SWATTN_MERGE_FUSED)):
         out, plan = sw.verify(t["q"], t["k"], t["v"], t["bt"], t["ctx"], w.n_q, w.window, w.scale, 4096,
-                              out_dtype=sw.SWATTN_F32, num_splits=S, workspace=ws)
+                              out_dtype=sw.SWATTN_F32, num_splits=S, workspace=ws, merge=merge)
         torch.cuda.synchronize()
-        assert plan.num_splits == S
+        assert plan.num_splits == S and plan.fused_merge == (merge == sw.SWATTN_MERGE_FUSED)
         got = out.cpu().numpy().astype(np.float64)
-        gu.check(got, ref, w.kv_dtype, True, label=f"reuse S={S}")
-        if S in first:
+        gu.check(got, ref, w.kv_dtype, True, label=f"reuse S={S} merge={merge}")
+        if S in first:   # the fused tail and the merge kernel combine with the same code
             assert np.array_equal(first[S], got), f"S={S} not reproducible"
         first[S] = got
+    # every call left the arrival counters at zero
+    assert int(ws[:sw.SWATTN_WORKSPACE_COUNTER_BYTES].count_nonzero()) == 0
 
 
 # ---------------------------------------------------------------------------
@@ -330,7 +370,9 @@ def test_graph_capture_replay():
     desc = sw.make_desc(t["q"], t["k"], t["bt"], 4096, num_splits=2)
     plan = sw.swattn_plan(desc, w.n_q, w.window)
     out = torch.empty(t["q"].shape, dtype=torch.bfloat16, device=gu.DEV)
+    assert plan.fused_merge == 1
     ws = torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device=gu.DEV)
+    sw.swattn_workspace_init(ws, ws.numel(), torch.cuda.current_stream().cuda_stream)
     sw.verify(t["q"], t["k"], t["v"], t["bt"], t["ctx"], w.n_q, w.window, w.scale, 4096,
               out=out, num_splits=2, workspace=ws)
     torch.cuda.synchronize()
