@@ -50,7 +50,7 @@ DESCRIPTIONS = {
                    "chunk of a 4096-token prompt, window 188, block 16, seed 5",
 }
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_verify_24x2kv_d256_w188_nq8.txt")
-KERNEL_SOURCES = ["partition_mfma.hip", "partition_valu.hip", "merge.hip", "kv_access.h",
+KERNEL_SOURCES = ["partition_mfma.hip", "partition_valu.hip", "merge.hip", "split_merge.h", "kv_access.h",
                   "swattn_internal.h", "plan.cpp", "api.cpp"]
 
 

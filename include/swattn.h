@@ -75,8 +75,9 @@ typedef enum {
 
 /* How the partials of a split launch (S > 1) are combined. */
 typedef enum {
-    SWATTN_MERGE_AUTO = 0,        /* fused for up to 4 splits when the launch has few enough
-                                     row chunks, else the merge kernel */
+    SWATTN_MERGE_AUTO = 0,        /* fused when a row chunk's partials are small (<= 16 KiB,
+                                     e.g. decode) and the launch has few enough row chunks,
+                                     else the merge kernel */
     SWATTN_MERGE_KERNEL = 1,      /* a separate merge kernel after the partition kernel */
     SWATTN_MERGE_FUSED = 2        /* the last partition workgroup of each row chunk combines;
                                      SWATTN_ERR_SHAPE when the launch has more row chunks

@@ -16,7 +16,7 @@ namespace {
 
 constexpr int64_t kFillTarget = 512;   // partition workgroups wanted in flight (2 per CU)
 constexpr int64_t kMfmaFewUnits = 16;  // matrix-core launches this small split every tile off
-constexpr int64_t kFusedMaxSplits = 4;  // automatic fused merge up to this many splits
+constexpr int64_t kFusedMaxPartialBytes = 16 * 1024;   // automatic fused merge up to this much per chunk
 
 bool dtype_in(int v, std::initializer_list<int> ok) {
     for (int o : ok)
@@ -123,14 +123,18 @@ swattn_status_t make_plan(const swattn_desc_t* d, int32_t n_q, int32_t window, i
     size_t ws = 0;
     if (S > 1) {
         // The last workgroup of each row chunk combines the partials (no second launch)
-        // when the chunks fit the counter region and there are at most kFusedMaxSplits
-        // partials per row; otherwise a merge kernel does.  Measured (MI355X, cold): one
-        // sequence of tiny decode at S = 3, 13.5 -> 12.6 us; full context 4096 at S = 8,
-        // 49 -> 54 us (one workgroup then reads 256 KiB of partials on its own).
+        // when the chunks fit the counter region and the chunk's partials are small
+        // (at most kFusedMaxPartialBytes: one workgroup reads them all, from past its
+        // L2); otherwise a merge kernel spreads the combination over many workgroups.
+        // Measured (MI355X, cold): tiny decode at S = 3 (1.5 KiB of partials), 13.5 ->
+        // 12.6 us; one layer of the verify step at S = 4 (128 KiB), +2 us per call;
+        // full context 4096 at S = 8 (256 KiB), 49 -> 54 us.
         const int64_t chunks_total = (int64_t)d->batch * d->num_kv_heads * row_chunks;
         if (d->merge == SWATTN_MERGE_FUSED && chunks_total > kMergeCounters) return SWATTN_ERR_SHAPE;
+        const int64_t chunk_partial_bytes = std::min<int64_t>(rows_per_chunk, R) * D * S * 4;
         fused = d->merge == SWATTN_MERGE_FUSED ||
-                (d->merge == SWATTN_MERGE_AUTO && chunks_total <= kMergeCounters && S <= kFusedMaxSplits);
+                (d->merge == SWATTN_MERGE_AUTO && chunks_total <= kMergeCounters &&
+                 chunk_partial_bytes <= kFusedMaxPartialBytes);
         if (!fused) {
             merge_grid = (rows_total + merge_rows_per_wg - 1) / merge_rows_per_wg;
             if (merge_grid > INT32_MAX) return SWATTN_ERR_SHAPE;

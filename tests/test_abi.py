@@ -107,10 +107,16 @@ def test_plan_variants_and_workspace():
                 o_bytes = -(-(units * R * S * D * 4) // 256) * 256
                 assert p.num_splits == S and p.variant == variant
                 assert p.workspace_bytes == sw.SWATTN_WORKSPACE_COUNTER_BYTES + o_bytes + units * R * S * 4
-                if merge == sw.SWATTN_MERGE_KERNEL or (merge == sw.SWATTN_MERGE_AUTO and S > 4):
-                    assert p.fused_merge == 0 and p.merge_grid == -(-(units * R) // (1024 // D))
-                else:
+                # automatic: fused only when a chunk's partials (rows x D x S x 4 B) fit 16 KiB
+                rows = 32 if variant == sw.SWATTN_VARIANT_MFMA else 8
+                small = rows * D * S * 4 <= 16 * 1024
+                if merge == sw.SWATTN_MERGE_FUSED or (merge == sw.SWATTN_MERGE_AUTO and small):
                     assert p.fused_merge == 1 and p.merge_grid == 0
+                else:
+                    assert p.fused_merge == 0 and p.merge_grid == -(-(units * R) // (1024 // D))
+    # decode-sized chunks: 2 rows x D 64 x 3 splits x 4 B = 1.5 KiB -> fused automatically
+    p = sw.swattn_plan(desc(head_dim=64, num_heads=2, num_kv_heads=1, batch=1, num_splits=3), 1, 188)
+    assert p.variant == sw.SWATTN_VARIANT_VALU and p.fused_merge == 1 and p.merge_grid == 0
     # more row chunks than counters: a merge kernel, and a forced fused merge is refused
     many = dict(batch=600, max_blocks_per_seq=16, max_ctx_len=256, num_splits=2)
     p = sw.swattn_plan(desc(**many), 8, 188)
@@ -158,7 +164,7 @@ def test_prefill_plan_caps_and_per_chunk_keys():
 def test_small_launches_split_per_tile():
     # one layer of the verify step: 2 units, 195 keys -> one split per 64-key tile
     p = sw.swattn_plan(desc(batch=1), 8, 188)
-    assert p.variant == sw.SWATTN_VARIANT_MFMA and p.num_splits == 4 and p.fused_merge == 1
+    assert p.variant == sw.SWATTN_VARIANT_MFMA and p.num_splits == 4 and p.merge_grid > 0
     # 24 layers stacked: 48 units, no split
     assert sw.swattn_plan(desc(batch=24), 8, 188).num_splits == 1
     # a forced split count still wins

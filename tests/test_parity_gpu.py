@@ -364,24 +364,25 @@ def test_workspace_reuse_across_split_counts():
 # ---------------------------------------------------------------------------
 # HIP graph capture and replay
 # ---------------------------------------------------------------------------
-def test_graph_capture_replay():
+@pytest.mark.parametrize("merge", [sw.SWATTN_MERGE_KERNEL, sw.SWATTN_MERGE_FUSED])
+def test_graph_capture_replay(merge):
     w, ref = gu.named("verify")
     t = gu.upload(w)
-    desc = sw.make_desc(t["q"], t["k"], t["bt"], 4096, num_splits=2)
+    desc = sw.make_desc(t["q"], t["k"], t["bt"], 4096, num_splits=2, merge=merge)
     plan = sw.swattn_plan(desc, w.n_q, w.window)
     out = torch.empty(t["q"].shape, dtype=torch.bfloat16, device=gu.DEV)
-    assert plan.fused_merge == 1
+    assert plan.fused_merge == (merge == sw.SWATTN_MERGE_FUSED)
     ws = torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device=gu.DEV)
     sw.swattn_workspace_init(ws, ws.numel(), torch.cuda.current_stream().cuda_stream)
     sw.verify(t["q"], t["k"], t["v"], t["bt"], t["ctx"], w.n_q, w.window, w.scale, 4096,
-              out=out, num_splits=2, workspace=ws)
+              out=out, num_splits=2, workspace=ws, merge=merge)
     torch.cuda.synchronize()
     eager = out.clone()
     out.zero_()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         sw.verify(t["q"], t["k"], t["v"], t["bt"], t["ctx"], w.n_q, w.window, w.scale, 4096,
-                  out=out, num_splits=2, workspace=ws)
+                  out=out, num_splits=2, workspace=ws, merge=merge)
     for rep in range(4):
         out.fill_(float("nan"))
         torch.cuda.synchronize()
