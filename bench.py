@@ -49,7 +49,12 @@ DESCRIPTIONS = {
     "prefill_512": "chunked prefill: 24 layers x (8 q / 2 kv heads), head_dim 256, bf16, the last 512-token "
                    "chunk of a 4096-token prompt, window 188, block 16, seed 5",
 }
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_verify_24x2kv_d256_w188_nq8.txt")
+# HBM-counter summaries (profiles/) of the workloads that have one
+TRAFFIC_SUMMARIES = {
+    "verify": os.path.join(ROOT, "profiles", "traffic_verify_24x2kv_d256_w188_nq8.txt"),
+    "batched_fp8": os.path.join(ROOT, "profiles", "traffic_batched_256seq_2kv_d256_e4m3_w188_nq8.txt"),
+    "batched_bf16": os.path.join(ROOT, "profiles", "traffic_batched_256seq_2kv_d256_bf16_w188_nq8.txt"),
+}
 KERNEL_SOURCES = ["partition_mfma.hip", "partition_valu.hip", "merge.hip", "split_merge.h", "kv_access.h",
                   "swattn_internal.h", "plan.cpp", "api.cpp"]
 
@@ -76,13 +81,14 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
-def read_traffic(calls_per_launch=1):
-    """HBM bytes per call from the committed counter summary, or None when it is
-    missing or was taken on other kernel sources."""
-    if not os.path.exists(TRAFFIC_SUMMARY):
+def read_traffic(workload="verify"):
+    """HBM bytes per call from the workload's committed counter summary, or None when
+    there is none or it was taken on other kernel sources."""
+    path = TRAFFIC_SUMMARIES.get(workload)
+    if path is None or not os.path.exists(path):
         return None
     kv = {}
-    with open(TRAFFIC_SUMMARY) as f:
+    with open(path) as f:
         for line in f:
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
@@ -340,7 +346,7 @@ def main():
 
     nbytes = algorithmic_bytes(w)
     achieved = nbytes / (cold_graph * 1e-6) / 1e9
-    traffic = read_traffic()
+    traffic = read_traffic(args.workload)
     line = {
         "metric": "verify-step us/call (W=188, n_q=8) + achieved HBM GB/s as % of MI355X peak",
         "value": round(cold_graph, 3),
