@@ -108,7 +108,8 @@ swattn_status_t attend(const swattn_desc_t* d, const void* q, const void* k_cach
         const int64_t tile64 = 64 * (int64_t)d->head_dim * kv_elt;
         const bool one_per_cu = 2 * (4 * tile64 + 14 * 1024) > 160 * 1024;
         const int64_t units = (int64_t)d->batch * d->num_kv_heads * plan.row_chunks * plan.num_splits;
-        p.tile_keys = (plan.variant == SWATTN_VARIANT_MFMA && one_per_cu && units > kComputeUnits) ? 32 : 64;
+        p.tile_keys = (plan.variant == SWATTN_VARIANT_MFMA && one_per_cu && units > kComputeUnits &&
+                       plan.rows_per_chunk == kMfmaRows) ? 32 : 64;
     }
 
     int err = plan.variant == SWATTN_VARIANT_MFMA ? launch_partition_mfma(p, plan.grid, stream)

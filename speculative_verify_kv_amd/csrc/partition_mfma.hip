@@ -53,7 +53,7 @@ typedef int int2_t __attribute__((ext_vector_type(2)));
 // KT = keys per tile.  64: two key halves of 32, one per wave pair, merged at the
 // end.  32: every wave takes all 32 keys of a tile and the waves split the output
 // columns instead, which halves the LDS a workgroup needs (no merge either).
-template <int D, bool FP8, int KT>
+template <int D, bool FP8, int KT, int RB = 2>
 struct Geo {
     static constexpr int kT = KT;
     static constexpr bool kSplitKeys = KT == 64;
@@ -78,7 +78,11 @@ struct Geo {
     // column sets: 64-key tiles split them only where one workgroup fills the CU;
     // 32-key tiles always split them in two (their waves do not split the keys)
     static constexpr int kND = kSplitKeys ? (kBlocks == 2 ? 1 : 2) : 2;
-    static constexpr int kNW = kSplitKeys ? 4 * kND : 4;    // waves: row blocks x key halves x column sets
+    // row blocks of 16 query rows per workgroup: 2, or 1 for launches that leave most
+    // CUs idle (two workgroups then share a 32-row chunk's keys, each with half the work)
+    static_assert(RB == 2 || (RB == 1 && KT == 64), "16-row chunks with 64-key tiles only");
+    static constexpr int kRows = 16 * RB;
+    static constexpr int kNW = kSplitKeys ? 2 * RB * kND : 4;    // waves: row blocks x key halves x column sets
     static constexpr int kNT = kNW * 64;
     static constexpr int kShare = 2 * kNiK / kNW;           // load instructions per wave per tile
     static_assert(kShare * kNW == 2 * kNiK && kShare <= 16, "loads split evenly over the waves");
@@ -167,9 +171,9 @@ __device__ __forceinline__ void dma16(const void* src, const void* lds_dst) {
 }
 #pragma clang diagnostic pop
 
-template <int D, bool FP8, bool OUT_F32, int KT>
-__global__ __launch_bounds__((Geo<D, FP8, KT>::kNT), (Geo<D, FP8, KT>::kBlocks)) void partition_mfma_kernel(PartitionParams p) {
-    using G = Geo<D, FP8, KT>;
+template <int D, bool FP8, bool OUT_F32, int KT, int RB>
+__global__ __launch_bounds__((Geo<D, FP8, KT, RB>::kNT), (Geo<D, FP8, KT, RB>::kBlocks)) void partition_mfma_kernel(PartitionParams p) {
+    using G = Geo<D, FP8, KT, RB>;
     constexpr int kT = KT;
     constexpr int NT = G::kNT;
     constexpr int KS = D / 32;                   // 32-dim k-steps of S^T = K Q^T
@@ -196,10 +200,10 @@ __global__ __launch_bounds__((Geo<D, FP8, KT>::kNT), (Geo<D, FP8, KT>::kBlocks))
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15;
     const int q4 = lane >> 4;
-    const int rb = wave & 1;                     // 16-row block
+    const int rb = RB == 2 ? wave & 1 : 0;      // 16-row block
     // key half of every tile (64-key tiles) and column set
-    const int kh = G::kSplitKeys ? (wave >> 1) & 1 : 0;
-    const int dh = G::kSplitKeys ? wave >> 2 : (wave >> 1) & 1;
+    const int kh = G::kSplitKeys ? (wave >> (RB - 1)) & 1 : 0;
+    const int dh = G::kSplitKeys ? wave >> RB : (wave >> 1) & 1;
 
     // grid (B * Hkv, row chunks, splits)
     const int s = blockIdx.z;
@@ -215,7 +219,7 @@ __global__ __launch_bounds__((Geo<D, FP8, KT>::kNT), (Geo<D, FP8, KT>::kBlocks))
     // Q^T operand of this lane: row rb*16 + l16, dims ks*32 + q4*8 .. +7, loaded
     // straight into registers.  A row past R loads a valid row instead; its window
     // is empty and it is never written.
-    const int qrow = rc * kMfmaRows + rb * 16 + l16;
+    const int qrow = rc * G::kRows + rb * 16 + l16;
     const bool qvalid = qrow < p.R;
     const int qi = qvalid ? qrow / p.G : 0;
     uint4 qreg[KS];
@@ -232,8 +236,8 @@ __global__ __launch_bounds__((Geo<D, FP8, KT>::kNT), (Geo<D, FP8, KT>::kBlocks))
     const int pos0 = seq_ok ? ctx - p.n_q : 0;             // position of query 0
     // The chunk's keys: the union of its rows' windows, queries qi_lo .. qi_hi, i.e.
     // positions [pos0 + qi_lo - W + 1, pos0 + qi_hi]; the split takes a 1/S share.
-    const int qi_lo = rc * kMfmaRows / p.G;
-    const int qi_hi = min(p.R - 1, rc * kMfmaRows + kMfmaRows - 1) / p.G;
+    const int qi_lo = rc * G::kRows / p.G;
+    const int qi_hi = min(p.R - 1, rc * G::kRows + G::kRows - 1) / p.G;
     const int u_lo = max(0, pos0 + qi_lo - p.window + 1);
     const int u_hi = pos0 + qi_hi + 1;                     // one past the last key
     int k0 = 0, nk = 0;
@@ -612,7 +616,7 @@ __global__ __launch_bounds__((Geo<D, FP8, KT>::kNT), (Geo<D, FP8, KT>::kBlocks))
 
 
 
-template <int D, int KT, bool WITH_FP8>
+template <int D, int KT, bool WITH_FP8, int RB>
 int launch_dk(const PartitionParams& p, int grid, hipStream_t st) {
     const bool fp8 = p.kv_dtype == SWATTN_FP8_E4M3;
     const bool of32 = p.out_dtype == SWATTN_F32;
@@ -620,20 +624,20 @@ int launch_dk(const PartitionParams& p, int grid, hipStream_t st) {
     if ((int64_t)grd.x * grd.y * grd.z != grid) return (int)hipErrorInvalidValue;
     if constexpr (WITH_FP8) {
         if (fp8) {
-            const dim3 blk(Geo<D, true, KT>::kNT);
+            const dim3 blk(Geo<D, true, KT, RB>::kNT);
             if (of32)
-                hipLaunchKernelGGL((partition_mfma_kernel<D, true, true, KT>), grd, blk, 0, st, p);
+                hipLaunchKernelGGL((partition_mfma_kernel<D, true, true, KT, RB>), grd, blk, 0, st, p);
             else
-                hipLaunchKernelGGL((partition_mfma_kernel<D, true, false, KT>), grd, blk, 0, st, p);
+                hipLaunchKernelGGL((partition_mfma_kernel<D, true, false, KT, RB>), grd, blk, 0, st, p);
             return (int)hipGetLastError();
         }
     }
     if (fp8) return (int)hipErrorInvalidValue;
-    const dim3 blk(Geo<D, false, KT>::kNT);
+    const dim3 blk(Geo<D, false, KT, RB>::kNT);
     if (of32)
-        hipLaunchKernelGGL((partition_mfma_kernel<D, false, true, KT>), grd, blk, 0, st, p);
+        hipLaunchKernelGGL((partition_mfma_kernel<D, false, true, KT, RB>), grd, blk, 0, st, p);
     else
-        hipLaunchKernelGGL((partition_mfma_kernel<D, false, false, KT>), grd, blk, 0, st, p);
+        hipLaunchKernelGGL((partition_mfma_kernel<D, false, false, KT, RB>), grd, blk, 0, st, p);
     return (int)hipGetLastError();
 }
 
@@ -642,9 +646,12 @@ int launch_d(const PartitionParams& p, int grid, hipStream_t st) {
     // 32-key tiles exist for the one case where a 64-key workgroup fills a CU's LDS:
     // bfloat16 caches with head_dim 256
     if constexpr (D == 256) {
-        if (p.tile_keys == 32 && p.kv_dtype == SWATTN_BF16) return launch_dk<D, 32, false>(p, grid, st);
+        if (p.tile_keys == 32 && p.kv_dtype == SWATTN_BF16 && p.rows_per_chunk == 32)
+            return launch_dk<D, 32, false, 2>(p, grid, st);
+        // 16-row chunks: bfloat16 and E4M3 caches with 64-key tiles
+        if (p.tile_keys == 64 && p.rows_per_chunk == 16) return launch_dk<D, 64, true, 1>(p, grid, st);
     }
-    if (p.tile_keys == 64) return launch_dk<D, 64, true>(p, grid, st);
+    if (p.tile_keys == 64 && p.rows_per_chunk == 32) return launch_dk<D, 64, true, 2>(p, grid, st);
     return (int)hipErrorInvalidValue;
 }
 

@@ -16,6 +16,7 @@ namespace {
 
 constexpr int64_t kFillTarget = 512;   // partition workgroups wanted in flight (2 per CU)
 constexpr int64_t kMfmaFewUnits = 16;  // matrix-core launches this small split every tile off
+constexpr bool kMfmaHalfRows = true;    // 16-row chunks for launches that leave CUs idle
 constexpr int64_t kFusedMaxPartialBytes = 16 * 1024;   // automatic fused merge up to this much per chunk
 
 bool dtype_in(int v, std::initializer_list<int> ok) {
@@ -99,6 +100,11 @@ swattn_status_t make_plan(const swattn_desc_t* d, int32_t n_q, int32_t window, i
             // 256 keys (four tiles) per split: a shorter chain per workgroup for the
             // cost of a merge (full context 1024: 30.7 -> 25.5 us at S = 4).
             S = std::max(s_min, std::min(kComputeUnits / units, (U + 255) / 256));
+        // Head_dim 256 launches that fit the CUs twice over take 16-row chunks: two
+        // workgroups share a 32-row chunk's keys (the same key range, each reading it
+        // whole), each with half the matrix work and LDS reads; the outputs stay
+        // disjoint, so nothing merges (one verify step of 24 layers: 15.0 -> 12.1 us).
+        if (kMfmaHalfRows && d->head_dim == 256 && 2 * units * S <= kComputeUnits) rows_per_chunk = kMfmaRows / 2;
     } else {
         rows_per_chunk = kValuRowsPerChunk;
         const int64_t row_chunks = (R + rows_per_chunk - 1) / rows_per_chunk;

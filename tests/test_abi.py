@@ -93,10 +93,11 @@ def test_plan_null_pointers():
 
 
 def test_plan_variants_and_workspace():
-    # verify step: 8 queries x GQA 4 = 32 rows -> matrix cores
+    # verify step: 8 queries x GQA 4 = 32 rows -> matrix cores; 48 units leave most CUs
+    # idle, so each 32-row chunk becomes two 16-row chunks (96 workgroups)
     p = sw.swattn_plan(desc(), 8, 188)
-    assert p.variant == sw.SWATTN_VARIANT_MFMA and p.rows_per_chunk == 32 and p.row_chunks == 1
-    assert p.grid == 24 * 2 * p.num_splits
+    assert p.variant == sw.SWATTN_VARIANT_MFMA and p.rows_per_chunk == 16 and p.row_chunks == 2
+    assert p.grid == 24 * 2 * 2 * p.num_splits
     R, D, units = 32, 256, 24 * 2
     # split plans: [counters][partial outputs][partial log2-sum-exps]; the partition
     # kernel combines the partials itself, or a merge kernel does when asked to
@@ -159,6 +160,22 @@ def test_prefill_plan_caps_and_per_chunk_keys():
     # full-context prefill: ceil(min(4096, 4096 + 8) / 512) = 8 splits
     p = sw.swattn_prefill_plan(desc(), 512, 4096)
     assert p.num_splits == 8 and p.merge_grid > 0
+
+
+def test_sixteen_row_chunks_only_while_the_grid_fits_the_cus():
+    # 48 units x 1 split, twice over, is 96 <= 256 workgroups: 16-row chunks
+    assert sw.swattn_plan(desc(), 8, 188).rows_per_chunk == 16
+    # one layer (2 units, 4 splits of one tile): 16 workgroups
+    p = sw.swattn_plan(desc(batch=1), 8, 188)
+    assert p.rows_per_chunk == 16 and p.num_splits == 4 and p.grid == 16
+    # full context (48 units x 4 or 8 splits) already fills the CUs: 32-row chunks
+    assert sw.swattn_plan(desc(max_ctx_len=1024), 8, 4096).rows_per_chunk == 32
+    assert sw.swattn_plan(desc(), 8, 4096).rows_per_chunk == 32
+    # 64 queries (8 chunks per KV head, 384 units) and head_dim 128: 32-row chunks
+    assert sw.swattn_plan(desc(), 64, 188).rows_per_chunk == 32
+    assert sw.swattn_plan(desc(head_dim=128), 8, 188).rows_per_chunk == 32
+    # the batched workload (512 units) keeps 32-row chunks
+    assert sw.swattn_plan(desc(batch=256), 8, 188).rows_per_chunk == 32
 
 
 def test_small_launches_split_per_tile():

@@ -248,6 +248,34 @@ def test_edge_shapes():
 
 
 # ---------------------------------------------------------------------------
+# launches that leave CUs idle take 16-row chunks (head_dim 256, two workgroups per
+# 32-row chunk): ragged row counts, both cache formats, splits, window edges
+# ---------------------------------------------------------------------------
+SIXTEEN = [
+    dict(B=3, H=8, Hkv=2, n_q=8, window=188, ctx=[195, 700, 4096], kv="bf16", S=(1, 2, 3)),
+    dict(B=2, H=8, Hkv=2, n_q=6, window=50, ctx=[6, 1000], kv="e4m3", S=(1, 2)),      # 24 rows: a ragged second chunk
+    dict(B=2, H=16, Hkv=2, n_q=3, window=7, ctx=[40, 300], kv="bf16", S=(1, 4)),       # G 8, 24 rows
+    dict(B=1, H=4, Hkv=1, n_q=4, window=188, ctx=[188], kv="e4m3", S=(1, 3)),          # exactly 16 rows
+]
+
+
+@pytest.mark.parametrize("k", range(len(SIXTEEN)))
+def test_sixteen_row_chunks(k):
+    c = dict(SIXTEEN[k])
+    kv = c.pop("kv")
+    splits = c.pop("S")
+    w = synth.make_workload(f"sixteen{k}", D=256, bs=16, seed=60 + k,
+                            kv_dtype=synth.workloads.E4M3 if kv == "e4m3" else synth.workloads.BF16, **c)
+    ref = gu.reference(w)
+    t = gu.upload(w)
+    for S in splits:
+        gu.log(f"[16-row] case {k} kv {kv} S={S}")
+        got, plan = gu.run(w, t, out_f32=True, num_splits=S)
+        assert plan.rows_per_chunk == 16 and plan.variant == sw.SWATTN_VARIANT_MFMA, plan.as_dict()
+        gu.check(got, ref, w.kv_dtype, True, label=f"sixteen{k} S={S}")
+
+
+# ---------------------------------------------------------------------------
 # launches with more units than CUs take 32-key tiles (bfloat16, head_dim 256)
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("S", [1, 2, 3])
