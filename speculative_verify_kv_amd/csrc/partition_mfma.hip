@@ -322,9 +322,13 @@ __global__ __launch_bounds__((Geo<D, FP8, KT, RB>::kNT), (Geo<D, FP8, KT, RB>::k
     // of qreg would count them as older: the Q rows (issued with ctx_len, so landed
     // by now) are waited for here instead, before any of them is issued.
     wait_vmcnt<0>();
-    // The first NS tiles go out together, one per stage.
+    // The first tiles go out together, one per stage: all NS where one workgroup has
+    // the CU, NS-1 where two share it (tile NS-1 then goes out with tile 0's scores:
+    // a wave whose loads stall at issue reaches its first tile sooner; batched E4M3,
+    // 512 workgroups: 21.4 -> 20.2 us).
+    constexpr int kPro = G::kBlocks == 2 ? NS - 1 : NS;
 #pragma unroll
-    for (int t = 0; t < NS; ++t)
+    for (int t = 0; t < kPro; ++t)
         if (t < ntiles) issue_range(t, 0, SH);
 
     float m_run = -INFINITY, l_run = 0.0f;   // row l16 of block rb, keys of half kh
@@ -337,7 +341,7 @@ __global__ __launch_bounds__((Geo<D, FP8, KT, RB>::kNT), (Geo<D, FP8, KT, RB>::k
     for (int t = 0; t < ntiles; ++t) {
         // This wave's loads of tile t have landed once only those of younger tiles are
         // pending: tiles t+1 .. t+ahead, issued before this point.
-        const int ahead = min(t == 0 ? NS - 1 : NS - 2, ntiles - 1 - t);
+        const int ahead = min(t == 0 ? kPro - 1 : NS - 2, ntiles - 1 - t);
         switch (ahead) {
             case 0: wait_vmcnt<0>(); break;
             case 1: wait_vmcnt<SH>(); break;
@@ -346,7 +350,7 @@ __global__ __launch_bounds__((Geo<D, FP8, KT, RB>::kNT), (Geo<D, FP8, KT, RB>::k
         }
         __syncthreads();   // B_t: tile t is in its stage for every wave; tile t-1's stage is free
         const int tn = t + NS - 1;                         // goes into tile t-1's stage
-        const bool prefetch = t >= 1 && tn < ntiles;
+        const bool prefetch = t >= kPro - (NS - 1) && tn < ntiles;
         // This wave's loads of tile tn go out between the matrix ops of the scores
         // below: a load instruction can stall its wave at issue while the memory
         // pipeline is busy, and the matrix ops already issued keep running meanwhile.
