@@ -276,6 +276,36 @@ def test_sixteen_row_chunks(k):
 
 
 # ---------------------------------------------------------------------------
+# many rows per KV head and more 32-row chunks than CUs (head_dim 256; 32-key tiles
+# for bfloat16 caches): ragged last chunks (a row block with no row), both cache
+# formats, GQA 4 and 8, short contexts and narrow windows
+# ---------------------------------------------------------------------------
+MANY_ROWS = [
+    dict(B=48, H=8, Hkv=2, n_q=20, window=188, ctx_range=(20, 1500), kv="bf16"),    # 80 rows: 32 + 32 + 16
+    dict(B=48, H=8, Hkv=2, n_q=17, window=100, ctx_range=(17, 400), kv="e4m3"),     # 68 rows: 32 + 32 + 4
+    dict(B=72, H=16, Hkv=2, n_q=8, window=7, ctx_range=(8, 300), kv="bf16"),        # G 8, 64 rows
+    dict(B=64, H=4, Hkv=1, n_q=64, window=188, ctx_range=(64, 900), kv="e4m3"),     # 256 rows
+]
+
+
+@pytest.mark.parametrize("k", range(len(MANY_ROWS)))
+def test_many_rows_per_kv_head(k):
+    c = dict(MANY_ROWS[k])
+    kv = c.pop("kv")
+    w = synth.make_workload(f"manyrows{k}", D=256, bs=16, seed=80 + k, ctx=None,
+                            kv_dtype=synth.workloads.E4M3 if kv == "e4m3" else synth.workloads.BF16, **c)
+    ref = gu.reference(w)
+    t = gu.upload(w)
+    gu.log(f"[many rows] case {k} kv {kv}")
+    got, plan = gu.run(w, t, out_f32=True)
+    assert plan.rows_per_chunk == 32 and plan.num_splits == 1 and plan.variant == sw.SWATTN_VARIANT_MFMA, \
+        plan.as_dict()
+    gu.check(got, ref, w.kv_dtype, True, label=f"manyrows{k}")
+    got16, _ = gu.run(w, t, out_f32=False)
+    gu.check(got16, ref, w.kv_dtype, False, label=f"manyrows{k} bf16 out")
+
+
+# ---------------------------------------------------------------------------
 # launches with more units than CUs take 32-key tiles (bfloat16, head_dim 256)
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("S", [1, 2, 3])
