@@ -48,6 +48,8 @@ DESCRIPTIONS = {
                    "n_q 64, 5% of Q rows x8, block 16, seed 3",
     "prefill_512": "chunked prefill: 24 layers x (8 q / 2 kv heads), head_dim 256, bf16, the last 512-token "
                    "chunk of a 4096-token prompt, window 188, block 16, seed 5",
+    "decode": "single-stream plain decode: 24 layers x (8 q heads / 2 kv heads), head_dim 256, bf16, "
+              "ctx 4096, window 188, n_q 1, paged block 16 (shuffled), seed 6",
 }
 # HBM-counter summaries (profiles/) of the workloads that have one
 TRAFFIC_SUMMARIES = {

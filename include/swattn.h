@@ -68,7 +68,7 @@ typedef enum {
 } swattn_status_t;
 
 typedef enum {
-    SWATTN_VARIANT_AUTO = 0,
+    SWATTN_VARIANT_AUTO = 0,      /* matrix cores for bf16 q with bf16/e4m3 kv, else vector ALU */
     SWATTN_VARIANT_VALU = 1,      /* fp32 vector-ALU partition kernel (any dtype) */
     SWATTN_VARIANT_MFMA = 2       /* bf16 matrix-core partition kernel (bf16 q, bf16/e4m3 kv) */
 } swattn_variant_t;

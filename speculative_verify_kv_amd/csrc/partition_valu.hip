@@ -1,16 +1,21 @@
 // Split-KV partition kernel on the vector ALUs, fp32 arithmetic (gfx950).
 //
-// Used when a KV head has fewer than 16 query rows (plain decode, n_q * H/Hkv
-// small) or when Q or the cache is float32, where a bf16 matrix-core tile would
-// either be mostly padding or lose precision.  One workgroup owns one
+// Used when Q or the cache is float32, where a bf16 matrix-core tile would lose
+// precision (and whenever the caller asks for it).  One workgroup owns one
 // (problem b, KV head g, 8-row chunk, KV split s) and at most 256 keys:
 //
+//   phase 0  the cache row of every key of the split, from the block table, into
+//            LDS (one pass, every key in parallel);
 //   phase 1  scores: 4 lanes per key, each dotting a quarter of the head
 //            dimension against the 8 rows held in LDS, two xor-shuffles to sum;
 //            the window mask (t - W, t] is applied here, scores kept in LDS;
 //   phase 2  exact softmax per row (one wave per row, max and sum by shuffles);
 //   phase 3  P V: each lane owns 4 consecutive dims of every row and a strided
 //            subset of the keys (coalesced V rows), partial sums meet in LDS.
+//
+// The kernel is a chain of dependent memory round trips, so phases 1 and 3 issue
+// the loads of several rounds (keys) before using any of them: one batch of loads
+// in flight per round trip instead of one round's.
 //
 // The result is the final output (S == 1) or a normalised partial plus its
 // log2-sum-exp for the merge kernel (S > 1).  Semantics: "The Fast Gemma
@@ -78,6 +83,7 @@ __device__ __forceinline__ void load_kv(const void* base, int64_t off, float* ds
     }
 }
 
+// Element offset of key j's cache row for KV head g, or -1 for a block id outside the pool.
 __device__ __forceinline__ int64_t valu_row_offset(const PartitionParams& p, int b, int g, int j) {
     const int blk = j / p.bs;
     const int off = j - blk * p.bs;
@@ -94,11 +100,14 @@ __global__ __launch_bounds__(kBlockThreads) void partition_valu_kernel(Partition
     constexpr int DPT = D / TPK;              // dims per lane in phase 1
     constexpr int QPR = D / 4;                // phase-3 lanes per row
     constexpr int KGR = kBlockThreads / QPR;  // phase-3 key groups
+    constexpr int RPB = D >= 128 ? 2 : 4;     // phase-1 rounds whose loads go out together
+    constexpr int U3 = 8;                     // phase-3 keys per lane whose loads go out together
 
     __shared__ float qs[RC][D];
     __shared__ float ps[RC][kValuMaxKeys];
     __shared__ __attribute__((aligned(16))) float red[KGR][RC][D];
     __shared__ float rstat[RC][2];
+    __shared__ int64_t roff[kValuMaxKeys];    // cache row of key k0 + kk (element offset), or -1
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -134,6 +143,9 @@ __global__ __launch_bounds__(kBlockThreads) void partition_valu_kernel(Partition
         osc = p.v_scale[g];
     }
 
+    // ---- phase 0: cache rows of the split's keys -> LDS --------------------------------
+    for (int kk = tid; kk < nk; kk += kBlockThreads) roff[kk] = valu_row_offset(p, b, g, k0 + kk);
+
     // ---- Q rows of this chunk -> LDS (float) ---------------------------------------
     for (int idx = tid; idx < RC * D; idx += kBlockThreads) {
         const int rr = idx / D, d = idx - rr * D;
@@ -154,23 +166,31 @@ __global__ __launch_bounds__(kBlockThreads) void partition_valu_kernel(Partition
     {
         const int slot = tid / TPK;
         const int part = tid % TPK;
-        for (int kr = 0; kr < nk; kr += KR) {
-            const int kk = kr + slot;
-            const bool valid = kk < nk;
-            const int j = k0 + kk;
-            float kv[DPT];
-            if (valid) {
-                const int64_t off = valu_row_offset(p, b, g, j);
+        for (int kb = 0; kb < nk; kb += RPB * KR) {
+        float kvb[RPB][DPT];
+#pragma unroll
+        for (int u = 0; u < RPB; ++u) {
+            const int kk = kb + u * KR + slot;
+            if (kk < nk) {
+                const int64_t off = roff[kk];
                 if (off >= 0) {
-                    load_kv<KVT, DPT>(p.k, off + part * DPT, kv);
+                    load_kv<KVT, DPT>(p.k, off + part * DPT, kvb[u]);
                 } else {
 #pragma unroll
-                    for (int e = 0; e < DPT; ++e) kv[e] = __builtin_nanf("");
+                    for (int e = 0; e < DPT; ++e) kvb[u][e] = __builtin_nanf("");
                 }
             } else {
 #pragma unroll
-                for (int e = 0; e < DPT; ++e) kv[e] = 0.0f;
+                for (int e = 0; e < DPT; ++e) kvb[u][e] = 0.0f;
             }
+        }
+#pragma unroll
+        for (int u = 0; u < RPB; ++u) {
+            const int kk = kb + u * KR + slot;
+            if (kb + u * KR >= nk) break;
+            const bool valid = kk < nk;
+            const int j = k0 + kk;
+            const float* kv = kvb[u];
             float dots[RC];
 #pragma unroll
             for (int rr = 0; rr < RC; ++rr) {
@@ -192,6 +212,7 @@ __global__ __launch_bounds__(kBlockThreads) void partition_valu_kernel(Partition
                     ps[rr][kk] = ok ? dots[rr] * sl2 : -INFINITY;
                 }
             }
+        }
         }
     }
     __syncthreads();
@@ -225,19 +246,31 @@ __global__ __launch_bounds__(kBlockThreads) void partition_valu_kernel(Partition
         float acc[RC][4];
 #pragma unroll
         for (int rr = 0; rr < RC; ++rr) acc[rr][0] = acc[rr][1] = acc[rr][2] = acc[rr][3] = 0.0f;
-        for (int kk = kgp; kk < nk; kk += KGR) {
-            const int64_t off = valu_row_offset(p, b, g, k0 + kk);
-            float v[4];
-            if (off >= 0) {
-                load_kv<KVT, 4>(p.v, off + dq, v);
-            } else {
-                v[0] = v[1] = v[2] = v[3] = __builtin_nanf("");
+        for (int kb = kgp; kb < nk; kb += U3 * KGR) {
+            float vb[U3][4];
+#pragma unroll
+            for (int u = 0; u < U3; ++u) {
+                const int kk = kb + u * KGR;
+                vb[u][0] = vb[u][1] = vb[u][2] = vb[u][3] = 0.0f;
+                if (kk < nk) {
+                    const int64_t off = roff[kk];
+                    if (off >= 0) {
+                        load_kv<KVT, 4>(p.v, off + dq, vb[u]);
+                    } else {
+                        vb[u][0] = vb[u][1] = vb[u][2] = vb[u][3] = __builtin_nanf("");
+                    }
+                }
             }
 #pragma unroll
-            for (int rr = 0; rr < RC; ++rr) {
-                const float pr = ps[rr][kk];
+            for (int u = 0; u < U3; ++u) {
+                const int kk = kb + u * KGR;
+                if (kk >= nk) break;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) acc[rr][e] = fmaf(pr, v[e], acc[rr][e]);
+                for (int rr = 0; rr < RC; ++rr) {
+                    const float pr = ps[rr][kk];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[rr][e] = fmaf(pr, vb[u][e], acc[rr][e]);
+                }
             }
         }
 #pragma unroll

@@ -199,6 +199,12 @@ def _c1():
                          recent=188 + 8 - 1)
 
 
+def _decode():
+    return make_workload("decode_24layers_h8kv2_d256_bf16_ctx4096_w188_nq1", B=24, H=8,
+                         Hkv=2, D=256, n_q=1, window=188, ctx=4096, bs=16, seed=6,
+                         recent=188)
+
+
 def _c2(ctx):
     return make_workload(f"fullctx_24layers_h8kv2_d256_bf16_ctx{ctx}_w4096_nq8", B=24,
                          H=8, Hkv=2, D=256, n_q=8, window=4096, ctx=ctx, bs=16, seed=2)
@@ -225,7 +231,8 @@ def _prefill(n_q):
 
 # The five workloads of the build: tiny decode, single-stream verify, the
 # full-context split-KV contrast (three lengths), wide verify and the batched
-# stress test (fp8 and bf16 KV).
+# stress test (fp8 and bf16 KV); then chunked prefill and single-stream plain
+# decode (the verify workload with one query per step).
 NAMED = {
     "tiny_decode": _c0,
     "verify": _c1,
@@ -236,6 +243,7 @@ NAMED = {
     "batched_fp8": lambda: _c4(E4M3),
     "batched_bf16": lambda: _c4(BF16),
     "prefill_512": lambda: _prefill(512),
+    "decode": _decode,
 }
 
 

@@ -115,9 +115,14 @@ def test_plan_variants_and_workspace():
                     assert p.fused_merge == 1 and p.merge_grid == 0
                 else:
                     assert p.fused_merge == 0 and p.merge_grid == -(-(units * R) // (1024 // D))
-    # decode-sized chunks: 2 rows x D 64 x 3 splits x 4 B = 1.5 KiB -> fused automatically
-    p = sw.swattn_plan(desc(head_dim=64, num_heads=2, num_kv_heads=1, batch=1, num_splits=3), 1, 188)
+    # decode-sized chunks: 2 rows x D 64 x 3 splits x 4 B = 1.5 KiB -> fused automatically,
+    # on the vector ALUs (float32 data) and on the matrix cores (bfloat16)
+    tiny = dict(head_dim=64, num_heads=2, num_kv_heads=1, batch=1, num_splits=3)
+    f32 = dict(q_dtype=sw.SWATTN_F32, kv_dtype=sw.SWATTN_F32, out_dtype=sw.SWATTN_F32)
+    p = sw.swattn_plan(desc(**tiny, **f32), 1, 188)
     assert p.variant == sw.SWATTN_VARIANT_VALU and p.fused_merge == 1 and p.merge_grid == 0
+    p = sw.swattn_plan(desc(**tiny), 1, 188)
+    assert p.variant == sw.SWATTN_VARIANT_MFMA and p.fused_merge == 1 and p.merge_grid == 0
     # more row chunks than counters: a merge kernel, and a forced fused merge is refused
     many = dict(batch=600, max_blocks_per_seq=16, max_ctx_len=256, num_splits=2)
     p = sw.swattn_plan(desc(**many), 8, 188)
@@ -125,8 +130,12 @@ def test_plan_variants_and_workspace():
     assert status(desc(merge=sw.SWATTN_MERGE_FUSED, **many)) == "SWATTN_ERR_SHAPE"
     assert sw.swattn_plan(desc(merge=sw.SWATTN_MERGE_FUSED, **dict(many, batch=512)), 8, 188).fused_merge == 1
     assert sw.swattn_workspace_bytes(desc(), 8, 188) == sw.swattn_plan(desc(), 8, 188).workspace_bytes
-    # decode: 4 rows -> vector ALU
+    # decode: 4 rows, bfloat16 -> matrix cores (a padded 16-row tile); float32 Q -> vector ALU
     p = sw.swattn_plan(desc(), 1, 188)
+    assert p.variant == sw.SWATTN_VARIANT_MFMA and p.rows_per_chunk == 16 and p.num_splits == 1
+    p = sw.swattn_plan(desc(kv_dtype=sw.SWATTN_FP8_E4M3, k_scale=16, v_scale=16), 1, 188)
+    assert p.variant == sw.SWATTN_VARIANT_MFMA
+    p = sw.swattn_plan(desc(q_dtype=sw.SWATTN_F32), 1, 188)
     assert p.variant == sw.SWATTN_VARIANT_VALU
     # float32 data -> vector ALU whatever the row count
     p = sw.swattn_plan(desc(q_dtype=sw.SWATTN_F32, kv_dtype=sw.SWATTN_F32), 64, 188)

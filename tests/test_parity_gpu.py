@@ -101,16 +101,22 @@ def test_fused_merge_equals_merge_kernel(key, variant):
         assert int(ws[:sw.SWATTN_WORKSPACE_COUNTER_BYTES].count_nonzero()) == 0
 
 
-def test_split_invariance_valu_decode():
+@pytest.mark.parametrize("variant", [sw.SWATTN_VARIANT_MFMA, sw.SWATTN_VARIANT_VALU])
+def test_split_invariance_decode(variant):
+    # plain decode (4 rows per KV head): a 16-row matrix-core tile with 12 padding rows,
+    # or the vector-ALU kernel
     w = synth.make_workload("decode", B=6, H=8, Hkv=2, D=256, n_q=1, window=188, ctx=[300, 188, 1, 4096, 189, 2000],
                             bs=16, seed=5, recent=188, max_blocks=256)
     ref = gu.reference(w)
     t = gu.upload(w)
     for S in (1, 2, 3):
-        gu.log(f"[valu splits] S={S}")
-        got, plan = gu.run(w, t, out_f32=True, num_splits=S, max_ctx=4096)
-        assert plan.variant == sw.SWATTN_VARIANT_VALU and plan.num_splits == S
-        gu.check(got, ref, w.kv_dtype, True, label=f"decode S={S}")
+        gu.log(f"[decode splits] variant {variant} S={S}")
+        got, plan = gu.run(w, t, out_f32=True, num_splits=S, max_ctx=4096, variant=variant)
+        assert plan.variant == variant and plan.num_splits == S
+        gu.check(got, ref, w.kv_dtype, True, label=f"decode variant {variant} S={S}")
+    auto, plan = gu.run(w, t, out_f32=False, max_ctx=4096)
+    assert plan.variant == sw.SWATTN_VARIANT_MFMA
+    gu.check(auto, ref, w.kv_dtype, False, label="decode auto")
 
 
 def test_variants_agree():
