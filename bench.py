@@ -56,6 +56,7 @@ TRAFFIC_SUMMARIES = {
     "verify": os.path.join(ROOT, "profiles", "traffic_verify_24x2kv_d256_w188_nq8.txt"),
     "batched_fp8": os.path.join(ROOT, "profiles", "traffic_batched_256seq_2kv_d256_e4m3_w188_nq8.txt"),
     "batched_bf16": os.path.join(ROOT, "profiles", "traffic_batched_256seq_2kv_d256_bf16_w188_nq8.txt"),
+    "decode": os.path.join(ROOT, "profiles", "traffic_decode_24x2kv_d256_w188_nq1.txt"),
 }
 KERNEL_SOURCES = ["partition_mfma.hip", "partition_valu.hip", "merge.hip", "split_merge.h", "kv_access.h",
                   "swattn_internal.h", "plan.cpp", "api.cpp"]
