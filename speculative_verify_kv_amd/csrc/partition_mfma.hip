@@ -1,10 +1,13 @@
 // Split-KV partition kernel on gfx950 matrix cores (bf16 MFMA 16x16x32).
 //
-// One workgroup owns one (problem b, KV head g, 32-row chunk, KV split s).  A KV
+// One workgroup owns one (problem b, KV head g, row chunk, KV split s).  A KV
 // head's query rows are its n_q queries times the H/Hkv heads that share it
 // (row r = i * G + head-in-group), so a verify step with n_q = 8 and GQA 4 is
-// one dense 32-row tile.  The split's keys are walked in tiles of 64 through a
-// two-stage LDS ring filled by direct global-to-LDS loads.
+// one dense 32-row tile.  Launches that leave most CUs idle take 16-row chunks,
+// each run by two workgroups that split the output columns (both load all K rows
+// and compute the same scores; each loads its half of every V row).  The split's
+// keys are walked in tiles of 64 (or 32) through an LDS ring filled by direct
+// global-to-LDS loads.
 //
 // Wave w owns 16 query rows (rb = w & 1) and one half of every tile's keys
 // (kh = (w >> 1) & 1), with an online softmax of its own, and a set of output
@@ -63,18 +66,28 @@ struct Geo {
     static constexpr int kCpr = kRowB / 16;                 // 16-byte chunks per row
     static constexpr int kRpi = 64 / kCpr;                  // rows per 64-lane load instruction (1 KiB)
     static constexpr int kNiK = kT / kRpi;                  // load instructions per K (or V) tile
-    static constexpr int kTileB = kT * kRowB;               // bytes of one K (or V) tile
+    static constexpr int kTileB = kT * kRowB;               // bytes of one K tile
     static_assert(kCpr >= 4 && kCpr <= 64 && kNiK * 1024 == kTileB, "tile geometry");
+    // 16-row chunks also split the output columns between two workgroups: each loads
+    // whole K rows (both compute the chunk's scores) and its own half of every V row.
+    static constexpr int kCS = RB == 1 ? 2 : 1;             // column splits
+    static constexpr int kRowBV = kRowB / kCS;              // bytes of a V row this workgroup loads
+    static constexpr int kCprV = kRowBV / 16;
+    static constexpr int kRpiV = 64 / kCprV;
+    static constexpr int kNiV = kT / kRpiV;                 // load instructions per V tile
+    static constexpr int kTileBV = kT * kRowBV;
+    static_assert(kCprV >= 4 && kNiV * 1024 == kTileBV, "V tile geometry");
+    static constexpr int kStageB = kTileB + kTileBV;
     // Stages of the K/V ring: four where two workgroups per CU still fit with them (up
     // to three tiles in flight absorb the tail latency of a loaded memory system),
     // else two.
-    static constexpr int kNS = 2 * (8 * kTileB + 14 * 1024) <= 160 * 1024 ? 4 : 2;
+    static constexpr int kNS = 2 * (4 * kStageB + 14 * 1024) <= 160 * 1024 ? 4 : 2;
     // Workgroups per CU that the LDS allows (the ring plus < 14 KiB of tables each,
     // 160 KiB per CU).  Where only one fits, the workgroup splits the output columns
     // across two wave sets (8 waves) so that every SIMD still holds two waves;
     // otherwise it has 4 waves.  Either way a SIMD runs two waves, so each may hold
     // 256 registers.
-    static constexpr int kBlocks = 2 * (2 * kNS * kTileB + 14 * 1024) <= 160 * 1024 ? 2 : 1;
+    static constexpr int kBlocks = 2 * (kNS * kStageB + 14 * 1024) <= 160 * 1024 ? 2 : 1;
     // column sets: 64-key tiles split them only where one workgroup fills the CU;
     // 32-key tiles always split them in two (their waves do not split the keys)
     static constexpr int kND = kSplitKeys ? (kBlocks == 2 ? 1 : 2) : 2;
@@ -84,20 +97,21 @@ struct Geo {
     static constexpr int kRows = 16 * RB;
     static constexpr int kNW = kSplitKeys ? 2 * RB * kND : 4;    // waves: row blocks x key halves x column sets
     static constexpr int kNT = kNW * 64;
-    static constexpr int kShare = 2 * kNiK / kNW;           // load instructions per wave per tile
-    static_assert(kShare * kNW == 2 * kNiK && kShare <= 16, "loads split evenly over the waves");
+    static constexpr int kShare = (kNiK + kNiV) / kNW;      // load instructions per wave per tile
+    static_assert(kShare * kNW == kNiK + kNiV && kShare <= 16, "loads split evenly over the waves");
     static_assert(kNS == 2 || kNS == 4, "ring of 2 or 4 stages");
     static_assert(kNS * kShare < 64, "a wave's loads in flight must fit the vmcnt counter");
     // K rows: chunk c of row k is stored at c ^ swz_k(k); 16 consecutive rows (the
     // 16 lanes of an A-operand read) land on distinct bank groups.
     static __device__ __forceinline__ int swz_k(int k) { return k & (kCpr >= 16 ? 15 : kCpr - 1); }
-    // V rows: a transpose read takes keys {4q + r} and {16 + 4q + r} of a 32-key
-    // half together (r < 4), so the swizzle separates r and bit 4 of the key.
+    // V rows (this workgroup's part of them): a transpose read takes keys {4q + r} and
+    // {16 + 4q + r} of a 32-key half together (r < 4), so the swizzle separates r and
+    // bit 4 of the key.
     static __device__ __forceinline__ int swz_v(int k) {
         if constexpr (FP8)
-            return ((k & 3) | ((k >> 2) & 4)) & (kCpr >= 8 ? 7 : 3);
+            return ((k & 3) | ((k >> 2) & 4)) & (kCprV >= 8 ? 7 : 3);
         else
-            return ((k & 3) << 1) & (kCpr - 1);
+            return ((k & 3) << 1) & (kCprV - 1);
     }
 };
 
@@ -177,7 +191,8 @@ __global__ __launch_bounds__((Geo<D, FP8, KT, RB>::kNT), (Geo<D, FP8, KT, RB>::k
     constexpr int kT = KT;
     constexpr int NT = G::kNT;
     constexpr int KS = D / 32;                   // 32-dim k-steps of S^T = K Q^T
-    constexpr int DH = D / G::kND;               // output columns of one wave set
+    constexpr int DC = D / G::kCS;               // output columns of this workgroup
+    constexpr int DH = DC / G::kND;              // output columns of one wave set
     constexpr int DB = DH / 16;                  // 16-column output tiles per wave
     constexpr int SH = G::kShare;                // this wave's loads per tile
     // P enters the PV product as one bfloat16 term for E4M3 caches (its rounding,
@@ -187,7 +202,7 @@ __global__ __launch_bounds__((Geo<D, FP8, KT, RB>::kNT), (Geo<D, FP8, KT, RB>::k
 
     constexpr int NS = G::kNS;
     __shared__ __attribute__((aligned(16))) unsigned char kst[NS][G::kTileB];
-    __shared__ __attribute__((aligned(16))) unsigned char vst[NS][G::kTileB];
+    __shared__ __attribute__((aligned(16))) unsigned char vst[NS][G::kTileBV];
     // source of every key's K and V row (a cache row, the zero row or the NaN row)
     __shared__ __attribute__((aligned(16))) const unsigned char* kptr[kMfmaMaxKeys];
     __shared__ __attribute__((aligned(16))) const unsigned char* vptr[kMfmaMaxKeys];
@@ -205,9 +220,10 @@ __global__ __launch_bounds__((Geo<D, FP8, KT, RB>::kNT), (Geo<D, FP8, KT, RB>::k
     const int kh = G::kSplitKeys ? (wave >> (RB - 1)) & 1 : 0;
     const int dh = G::kSplitKeys ? wave >> RB : (wave >> 1) & 1;
 
-    // grid (B * Hkv, row chunks, splits)
+    // grid (B * Hkv, row chunks x column splits, splits)
     const int s = blockIdx.z;
-    const int rc = blockIdx.y;
+    const int rc = blockIdx.y / G::kCS;
+    const int cs = blockIdx.y - rc * G::kCS;     // this workgroup's columns: cs*DC .. +DC-1
     const int g = blockIdx.x % p.Hkv;
     const int b = blockIdx.x / p.Hkv;
 
@@ -283,16 +299,22 @@ __global__ __launch_bounds__((Geo<D, FP8, KT, RB>::kNT), (Geo<D, FP8, KT, RB>::k
     //      first, then V tile); instruction i fills rows (i % kNiK)*kRpi .. +kRpi-1, and
     //      lane l of it chunk l % kCpr of row (i % kNiK)*kRpi + l / kCpr
     const int rsub = lane / G::kCpr;
-    const int pch = lane % G::kCpr;              // LDS chunk this lane fills
+    const int pch = lane % G::kCpr;              // LDS chunk this lane fills (K)
+    const int rsub_v = lane / G::kCprV;
+    const int pch_v = lane % G::kCprV;           // (V)
     // captures by value: a by-reference closure pins the captured locals in scratch
     auto rows_of = [=](int t, const unsigned char** src) __attribute__((always_inline)) {   // this wave's SH source rows of tile t
 #pragma unroll
         for (int j = 0; j < SH; ++j) {
             const int ins = wave * SH + j;
             const bool is_v = ins >= G::kNiK;
-            const int row = (is_v ? ins - G::kNiK : ins) * G::kRpi + rsub;
-            const int ch = pch ^ (is_v ? G::swz_v(row) : G::swz_k(row));
-            src[j] = (is_v ? vptr : kptr)[t * kT + row] + ch * 16;
+            if (is_v) {
+                const int row = (ins - G::kNiK) * G::kRpiV + rsub_v;
+                src[j] = vptr[t * kT + row] + cs * G::kRowBV + ((pch_v ^ G::swz_v(row)) << 4);
+            } else {
+                const int row = ins * G::kRpi + rsub;
+                src[j] = kptr[t * kT + row] + ((pch ^ G::swz_k(row)) << 4);
+            }
         }
     };
     // loads j0 .. j1-1 of this wave's share of tile t
@@ -493,7 +515,7 @@ __global__ __launch_bounds__((Geo<D, FP8, KT, RB>::kNT), (Geo<D, FP8, KT, RB>::k
                 const int r = l16 >> 1;
                 const int kr = kbase_t + (r & 3) + q4 * 4 + (r >> 2) * 16;
                 const int d = d0 + 8 * (l16 & 1);
-                const int off = kr * G::kRowB + (((d >> 4) ^ G::swz_v(kr)) << 4) + (d & 15);
+                const int off = kr * G::kRowBV + (((d >> 4) ^ G::swz_v(kr)) << 4) + (d & 15);
                 const int2_t w = __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDS_PTR(int2_t, vc + off));
                 a = make_uint4((uint32_t)w[0], (uint32_t)w[1], 0u, 0u);   // converted at use
             } else {
@@ -504,7 +526,7 @@ __global__ __launch_bounds__((Geo<D, FP8, KT, RB>::kNT), (Geo<D, FP8, KT, RB>::k
                 for (int hh = 0; hh < 2; ++hh) {
                     const int kr = kbase_t + hh * 16 + q4 * 4 + (l16 >> 2);
                     const int d = d0 + 4 * (l16 & 3);
-                    const int off = kr * G::kRowB + (((d >> 3) ^ G::swz_v(kr)) << 4) + (d & 7) * 2;
+                    const int off = kr * G::kRowBV + (((d >> 3) ^ G::swz_v(kr)) << 4) + (d & 7) * 2;
                     const short4_t v4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(short4_t, vc + off));
                     wv[2 * hh] = (uint32_t)(uint16_t)v4[0] | ((uint32_t)(uint16_t)v4[1] << 16);
                     wv[2 * hh + 1] = (uint32_t)(uint16_t)v4[2] | ((uint32_t)(uint16_t)v4[3] << 16);
@@ -535,7 +557,7 @@ __global__ __launch_bounds__((Geo<D, FP8, KT, RB>::kNT), (Geo<D, FP8, KT, RB>::k
         const float poison = seq_ok ? 0.0f : __builtin_nanf("");
         const float inv = l_run == 0.0f ? 0.0f : out_scale / l_run;   // a NaN sum must propagate
         const int h = g * p.G + (qrow - qi * p.G);
-        const int64_t obase = (((int64_t)b * p.n_q + qi) * p.H + h) * D + dcol0 + q4 * 4;
+        const int64_t obase = (((int64_t)b * p.n_q + qi) * p.H + h) * D + cs * DC + dcol0 + q4 * 4;
         const int64_t prow = (((int64_t)b * p.Hkv + g) * p.S + s) * p.R + qrow;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
@@ -550,10 +572,10 @@ __global__ __launch_bounds__((Geo<D, FP8, KT, RB>::kNT), (Geo<D, FP8, KT, RB>::k
                     *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + obase + db * 16) = wq;
                 }
             } else {
-                store_partial4(p, p.ws_o + prow * D + dcol0 + db * 16 + q4 * 4, v);
+                store_partial4(p, p.ws_o + prow * D + cs * DC + dcol0 + db * 16 + q4 * 4, v);
             }
         }
-        if (p.S > 1 && dh == 0 && q4 == 0)
+        if (p.S > 1 && cs == 0 && dh == 0 && q4 == 0)
             store_partial1(p, p.ws_lse + prow, (l_run == 0.0f ? -INFINITY : m_run + log2f(l_run)) + poison);
         }
     } else {
@@ -590,7 +612,7 @@ __global__ __launch_bounds__((Geo<D, FP8, KT, RB>::kNT), (Geo<D, FP8, KT, RB>::k
     const float poison = seq_ok ? 0.0f : __builtin_nanf("");
     const float inv = l_all == 0.0f ? 0.0f : out_scale / l_all;   // a NaN sum must propagate
     const int h = g * p.G + (qrow - qi * p.G);
-    const int64_t obase = (((int64_t)b * p.n_q + qi) * p.H + h) * D + mcol + q4 * 4;
+    const int64_t obase = (((int64_t)b * p.n_q + qi) * p.H + h) * D + cs * DC + mcol + q4 * 4;
     const int64_t prow = (((int64_t)b * p.Hkv + g) * p.S + s) * p.R + qrow;
 #pragma unroll
     for (int db = 0; db < DB / 2; ++db) {
@@ -606,16 +628,16 @@ __global__ __launch_bounds__((Geo<D, FP8, KT, RB>::kNT), (Geo<D, FP8, KT, RB>::k
                 *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + obase + db * 16) = wq;
             }
         } else {
-            store_partial4(p, p.ws_o + prow * D + mcol + db * 16 + q4 * 4, v);
+            store_partial4(p, p.ws_o + prow * D + cs * DC + mcol + db * 16 + q4 * 4, v);
         }
     }
-    if (p.S > 1 && kh == 0 && dh == 0 && q4 == 0)
+    if (p.S > 1 && cs == 0 && kh == 0 && dh == 0 && q4 == 0)
         store_partial1(p, p.ws_lse + prow, (l_all == 0.0f ? -INFINITY : m_all + log2f(l_all)) + poison);
     }
     }
 
     // ---- split launches: the last workgroup of the row chunk combines the partials
-    if (p.counters != nullptr) merge_if_last<D, OUT_F32, NT>(p, b, g, rc);
+    if (p.counters != nullptr) merge_if_last<D, OUT_F32, NT>(p, b, g, rc, p.S * G::kCS);
 }
 
 
@@ -624,7 +646,7 @@ template <int D, int KT, bool WITH_FP8, int RB>
 int launch_dk(const PartitionParams& p, int grid, hipStream_t st) {
     const bool fp8 = p.kv_dtype == SWATTN_FP8_E4M3;
     const bool of32 = p.out_dtype == SWATTN_F32;
-    const dim3 grd((unsigned)(p.B * p.Hkv), (unsigned)p.row_chunks, (unsigned)p.S);
+    const dim3 grd((unsigned)(p.B * p.Hkv), (unsigned)(p.row_chunks * Geo<D, false, KT, RB>::kCS), (unsigned)p.S);
     if ((int64_t)grd.x * grd.y * grd.z != grid) return (int)hipErrorInvalidValue;
     if constexpr (WITH_FP8) {
         if (fp8) {

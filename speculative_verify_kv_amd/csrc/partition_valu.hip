@@ -309,9 +309,9 @@ __global__ __launch_bounds__(kBlockThreads) void partition_valu_kernel(Partition
     // split launches: the last workgroup of the row chunk combines the partials
     if (p.counters != nullptr) {
         if (p.out_dtype == SWATTN_F32)
-            merge_if_last<D, true, kBlockThreads>(p, b, g, rc);
+            merge_if_last<D, true, kBlockThreads>(p, b, g, rc, p.S);
         else
-            merge_if_last<D, false, kBlockThreads>(p, b, g, rc);
+            merge_if_last<D, false, kBlockThreads>(p, b, g, rc, p.S);
     }
 }
 

@@ -157,7 +157,8 @@ __device__ __forceinline__ void store_out4(void* out, int64_t oi, f32x4_t v) {
 // partials of the chunk's rows and writes the output, so no merge kernel runs.
 //
 // Arrival is counted in p.counters[(b * Hkv + g) * row_chunks + rc], which must be
-// zero when the call starts; the last workgroup sets it back to zero.  The partials
+// zero when the call starts; the last of the `arrivals` workgroups that write the
+// chunk's partials (its splits, times its column splits) sets it back to zero.  The partials
 // were written with device-coherent stores (store_partial4/1); every wave waits until
 // its stores have completed before the workgroup counts itself (an agent-scope atomic
 // add), and the workgroup that counts last reads the partials with device-coherent
@@ -166,14 +167,14 @@ __device__ __forceinline__ void store_out4(void* out, int64_t oi, f32x4_t v) {
 // microseconds per launch.)  Every thread of every workgroup must call this: it
 // contains barriers.
 template <int D, bool OUT_F32, int NT>
-__device__ __forceinline__ void merge_if_last(const PartitionParams& p, int b, int g, int rc) {
+__device__ __forceinline__ void merge_if_last(const PartitionParams& p, int b, int g, int rc, int arrivals) {
     __shared__ int last;
     __builtin_amdgcn_s_waitcnt(0);           // this wave's partial stores are done
     __syncthreads();
     if (threadIdx.x == 0) {
         int* c = p.counters + ((int64_t)b * p.Hkv + g) * p.row_chunks + rc;
         const int arrived = __hip_atomic_fetch_add(c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1;
-        const bool is_last = arrived == p.S;
+        const bool is_last = arrived == arrivals;
         // every split has counted: ready for the next call
         if (is_last) __hip_atomic_store(c, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         last = is_last;

@@ -94,10 +94,11 @@ def test_plan_null_pointers():
 
 def test_plan_variants_and_workspace():
     # verify step: 8 queries x GQA 4 = 32 rows -> matrix cores; 48 units leave most CUs
-    # idle, so each 32-row chunk becomes two 16-row chunks (96 workgroups)
+    # idle, so each 32-row chunk becomes two 16-row chunks, each run by two workgroups
+    # (output column halves): 192 workgroups
     p = sw.swattn_plan(desc(), 8, 188)
     assert p.variant == sw.SWATTN_VARIANT_MFMA and p.rows_per_chunk == 16 and p.row_chunks == 2
-    assert p.grid == 24 * 2 * 2 * p.num_splits
+    assert p.grid == 24 * 2 * 2 * 2 * p.num_splits
     R, D, units = 32, 256, 24 * 2
     # split plans: [counters][partial outputs][partial log2-sum-exps]; the partition
     # kernel combines the partials itself, or a merge kernel does when asked to
@@ -172,11 +173,18 @@ def test_prefill_plan_caps_and_per_chunk_keys():
 
 
 def test_sixteen_row_chunks_only_while_the_grid_fits_the_cus():
-    # 48 units x 1 split, twice over, is 96 <= 256 workgroups: 16-row chunks
+    # 48 units x 1 split, four times over (two 16-row chunks, two column halves each), is
+    # 192 <= 256 workgroups: 16-row chunks
     assert sw.swattn_plan(desc(), 8, 188).rows_per_chunk == 16
-    # one layer (2 units, 4 splits of one tile): 16 workgroups
+    # one layer (2 units, 4 splits of one tile): 32 workgroups
     p = sw.swattn_plan(desc(batch=1), 8, 188)
-    assert p.rows_per_chunk == 16 and p.num_splits == 4 and p.grid == 16
+    assert p.rows_per_chunk == 16 and p.num_splits == 4 and p.grid == 32
+    # 96 units (48 problems) four times over is 384 > 256: 32-row chunks
+    p = sw.swattn_plan(desc(batch=48), 8, 188)
+    assert p.rows_per_chunk == 32 and p.grid == 48 * 2
+    # 64 units: 16-row chunks again (256 workgroups)
+    p = sw.swattn_plan(desc(batch=32), 8, 188)
+    assert p.rows_per_chunk == 16 and p.grid == 256
     # full context (48 units x 4 or 8 splits) already fills the CUs: 32-row chunks
     assert sw.swattn_plan(desc(max_ctx_len=1024), 8, 4096).rows_per_chunk == 32
     assert sw.swattn_plan(desc(), 8, 4096).rows_per_chunk == 32
