@@ -95,7 +95,14 @@ struct Geo {
     // CUs idle (two workgroups then share a 32-row chunk's keys, each with half the work)
     static_assert(RB == 2 || (RB == 1 && KT == 64), "16-row chunks with 64-key tiles only");
     static constexpr int kRows = 16 * RB;
-    static constexpr int kNW = kSplitKeys ? 2 * RB * kND : 4;    // waves: row blocks x key halves x column sets
+    static constexpr int kNWc = kSplitKeys ? 2 * RB * kND : 4;   // compute waves: row blocks x key halves x column sets
+    // 16-row workgroups (one per CU for bfloat16) add as many loader waves, which take
+    // their share of every tile's loads and do no arithmetic: a workgroup's load rate
+    // grows with the number of waves issuing its loads (a memory-only probe of the
+    // verify step's 147 KB per workgroup: 10.5 us with 4 waves, 8.2 us with 8; the
+    // verify step itself: 9.7 -> 8.7 us warm, cold unchanged).
+    static constexpr int kNL = RB == 1 ? kNWc : 0;
+    static constexpr int kNW = kNWc + kNL;
     static constexpr int kNT = kNW * 64;
     static constexpr int kShare = (kNiK + kNiV) / kNW;      // load instructions per wave per tile
     static_assert(kShare * kNW == kNiK + kNiV && kShare <= 16, "loads split evenly over the waves");
@@ -213,12 +220,14 @@ __global__ __launch_bounds__((Geo<D, FP8, KT, RB>::kNT), (Geo<D, FP8, KT, RB>::k
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool loader = G::kNL > 0 && wave >= G::kNWc;   // loads and barriers only
+    const int cw = loader ? 0 : wave;            // compute-wave index (loaders mirror wave 0)
     const int l16 = lane & 15;
     const int q4 = lane >> 4;
-    const int rb = RB == 2 ? wave & 1 : 0;      // 16-row block
+    const int rb = RB == 2 ? cw & 1 : 0;        // 16-row block
     // key half of every tile (64-key tiles) and column set
-    const int kh = G::kSplitKeys ? (wave >> (RB - 1)) & 1 : 0;
-    const int dh = G::kSplitKeys ? wave >> RB : (wave >> 1) & 1;
+    const int kh = G::kSplitKeys ? (cw >> (RB - 1)) & 1 : 0;
+    const int dh = G::kSplitKeys ? cw >> RB : (cw >> 1) & 1;
 
     // grid (B * Hkv, row chunks x column splits, splits)
     const int s = blockIdx.z;
@@ -244,7 +253,7 @@ __global__ __launch_bounds__((Geo<D, FP8, KT, RB>::kNT), (Geo<D, FP8, KT, RB>::k
         const uint16_t* qp =
             reinterpret_cast<const uint16_t*>(p.q) + (((int64_t)b * p.n_q + qi) * p.H + h) * D + q4 * 8;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qreg[ks] = ld_global_16(qp + ks * 32);
+        for (int ks = 0; ks < KS; ++ks) qreg[ks] = loader ? make_uint4(0u, 0u, 0u, 0u) : ld_global_16(qp + ks * 32);
     }
 
     const int ctx = p.ctx_len[b];
@@ -383,6 +392,13 @@ __global__ __launch_bounds__((Geo<D, FP8, KT, RB>::kNT), (Geo<D, FP8, KT, RB>::k
             const bool is_v = ins >= G::kNiK;
             dma16(from, (is_v ? vst[tn % NS] : kst[tn % NS]) + (is_v ? ins - G::kNiK : ins) * 1024);
         };
+        if (loader) {
+            if (prefetch) {
+#pragma unroll
+                for (int j = 0; j < SH; ++j) load_one(j, src[j]);
+            }
+            continue;
+        }
         constexpr int kPerStep = (SH + KS - 1) / KS;        // loads after each k-step's matrix ops
         const unsigned char* kc = kst[t % NS];
         const unsigned char* vc = vst[t % NS];
@@ -553,7 +569,7 @@ __global__ __launch_bounds__((Geo<D, FP8, KT, RB>::kNT), (Geo<D, FP8, KT, RB>::k
 
     if constexpr (!G::kSplitKeys) {
         // ---- every wave holds all keys of its rows: normalise and write its columns
-        if (qrow < p.R) {
+        if (!loader && qrow < p.R) {
         const float poison = seq_ok ? 0.0f : __builtin_nanf("");
         const float inv = l_run == 0.0f ? 0.0f : out_scale / l_run;   // a NaN sum must propagate
         const int h = g * p.G + (qrow - qi * p.G);
@@ -585,7 +601,7 @@ __global__ __launch_bounds__((Geo<D, FP8, KT, RB>::kNT), (Geo<D, FP8, KT, RB>::k
     // other half of its O^T, with its (max, sum), to its partner (rb, 1 - kh, dh).
     __syncthreads();   // every wave is done with the stages
     float* xo = reinterpret_cast<float*>(&kst[0][0]);          // [rb][writer kh][dh][16 rows][DH/2]
-    {
+    if (!loader) {
         float* dst = xo + (((rb * 2 + kh) * G::kND + dh) * 16 + l16) * (DH / 2);
 #pragma unroll
         for (int db = 0; db < DB / 2; ++db) {
@@ -608,7 +624,7 @@ __global__ __launch_bounds__((Geo<D, FP8, KT, RB>::kNT), (Geo<D, FP8, KT, RB>::k
     const float* src = xo + (((rb * 2 + (1 - kh)) * G::kND + dh) * 16 + l16) * (DH / 2);
     const int mcol = dcol0 + kh * (DH / 2);                    // the columns this wave writes
 
-    if (qrow < p.R) {
+    if (!loader && qrow < p.R) {
     const float poison = seq_ok ? 0.0f : __builtin_nanf("");
     const float inv = l_all == 0.0f ? 0.0f : out_scale / l_all;   // a NaN sum must propagate
     const int h = g * p.G + (qrow - qi * p.G);
