@@ -65,14 +65,25 @@ def test_split_invariance_and_determinism_mfma():
         assert np.abs(outs[S] - outs[1]).max() <= 2e-3
 
 
-@pytest.mark.parametrize("key,variant", [("verify", sw.SWATTN_VARIANT_MFMA), ("batched_fp8", sw.SWATTN_VARIANT_MFMA),
+def _workload_and_reference(key):
+    if key == "one_layer":
+        # one layer of the verify step (2 units): every split count keeps 16-row chunks,
+        # each run by two workgroups (column halves), so a chunk waits for S x 2 arrivals
+        w = synth.make_workload("one_layer", B=1, H=8, Hkv=2, D=256, n_q=8, window=188, ctx=4096, bs=16, seed=7,
+                                recent=195)
+        return w, gu.reference(w)
+    return gu.named(key)
+
+
+@pytest.mark.parametrize("key,variant", [("verify", sw.SWATTN_VARIANT_MFMA), ("one_layer", sw.SWATTN_VARIANT_MFMA),
+                                         ("batched_fp8", sw.SWATTN_VARIANT_MFMA),
                                          ("tiny_decode", sw.SWATTN_VARIANT_VALU), ("verify", sw.SWATTN_VARIANT_VALU)])
 def test_fused_merge_equals_merge_kernel(key, variant):
     """The last partition workgroup of a row chunk combines the partials with the same
     code as the merge kernel: identical outputs.  Calls alternate between two query
     sets on one workspace, so a partial read before its writer's stores landed, or a
     counter not reset, shows as a mismatch."""
-    w, ref = gu.named(key)
+    w, ref = _workload_and_reference(key)
     t = gu.upload(w)
     q_sets = [t["q"], (-t["q"]).contiguous()]
     S_list = (2, 3, 4, 8) if key != "batched_fp8" else (2,)
@@ -90,6 +101,8 @@ def test_fused_merge_equals_merge_kernel(key, variant):
         gu.log(f"[fused merge] {key} variant={variant} S={S}")
         kern = [call(q, S, sw.SWATTN_MERGE_KERNEL, None) for q in q_sets]
         assert kern[0][1].merge_grid > 0 and kern[0][1].fused_merge == 0
+        if key == "one_layer":
+            assert kern[0][1].rows_per_chunk == 16 and kern[0][1].grid == 2 * 2 * 2 * S
         gu.check(kern[0][0], ref, w.kv_dtype, True, label=f"{key} S={S} merge kernel")
         plan = kern[0][1]
         ws = torch.zeros(plan.workspace_bytes, dtype=torch.uint8, device=gu.DEV)
