@@ -9,23 +9,25 @@
 // keys are walked in tiles of 64 (or 32) through an LDS ring filled by direct
 // global-to-LDS loads.
 //
-// Wave w owns 16 query rows (rb = w & 1) and one half of every tile's keys
-// (kh = (w >> 1) & 1), with an online softmax of its own, and a set of output
-// columns (dh = w >> 2): all of them when two workgroups fit in a CU's LDS (4
-// waves), half of them otherwise (8 waves, so that a SIMD still runs two).  Per
-// tile:
+// With 64-key tiles, compute wave w owns 16 query rows (a row block), one 32-key
+// half of every tile's keys, with an online softmax of its own, and a set of the
+// workgroup's output columns: all of them when two workgroups fit in a CU's LDS,
+// half of them otherwise (so that a SIMD still runs two waves).  With 32-key tiles
+// every wave takes all keys of its row block and the waves split the columns.
+// 16-row workgroups add as many loader waves, which only load and pass barriers.
+// Per tile:
 //   S^T = K . Q^T        matrix cores; K rows from LDS, Q^T in registers for the
 //                        whole call; window (t - W, t] mask and scale applied
 //   softmax              in registers: row max and sum across the four 16-lane
 //                        groups with lane-swap permutes; P = 2^(S - max) as two
-//                        bf16 terms (hi + lo)
+//                        bf16 terms (hi + lo) for bfloat16 caches, one for E4M3
 //   O^T += V^T . P^T     matrix cores; P^T straight from registers, V^T from the
 //                        row-major V tile by LDS transpose reads
-// While it works on tile t, each wave issues a quarter of tile t+1's loads into
-// the other stage, in two halves (a wave keeps about eight loads in flight).  One
-// barrier per tile hands a landed stage to all waves and frees the stage of tile
-// t-1.  At the end the two key halves of each row block merge their (max, sum, O)
-// through LDS.
+// The ring has two stages (four where they are small).  While the waves work on
+// tile t, each issues its share of the loads of the tile NS-1 ahead into the stage
+// that tile t-1 held, between the score matrix ops.  One barrier per tile hands a
+// landed stage to all waves and frees the stage of tile t-1.  At the end the two
+// key halves of each row block merge their (max, sum, O) through LDS.
 //
 // Cache rows sit in LDS with their 16-byte chunks XOR-swizzled by row so that
 // the matrix-operand reads of consecutive keys hit distinct LDS banks.  Keys
