@@ -28,6 +28,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import statistics
 import sys
 import time
@@ -76,11 +77,20 @@ def algorithmic_bytes(w, out_elt=None):
             + w.B * w.n_q * w.H * w.D * o_elt)
 
 
+def _code_only(text):
+    """Source text without // and /* */ comments, trailing blanks and empty lines (the
+    kernel sources hold no comment markers inside string literals)."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def source_hash():
+    """Hash of the code (not the comments) of the sources that decide the kernels' traffic."""
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "speculative_verify_kv_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "speculative_verify_kv_amd", "csrc", name), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
