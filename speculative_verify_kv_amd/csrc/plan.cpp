@@ -95,11 +95,16 @@ swattn_status_t make_plan(const swattn_desc_t* d, int32_t n_q, int32_t window, i
         const int64_t units = (int64_t)d->batch * d->num_kv_heads * chunks;
         if (d->num_splits > 0)
             S = clamp64(d->num_splits, s_min, std::max<int64_t>(s_min, (U + 15) / 16));
-        else if (units <= kMfmaFewUnits)
+        else if (units <= kMfmaFewUnits) {
             // A launch this small leaves most CUs idle and its time is one workgroup's
             // chain of tiles: one tile (64 keys) per split shortens the chain more than
-            // the merge costs (one layer's verify step: 436 -> 367 us per 24 layers).
+            // the merge costs when the partials are small enough for the fused merge
+            // (one layer of plain decode: 9.5 -> 7.3 us).  Behind a merge kernel the
+            // split costs more than it saves (the 24-layer step of per-layer verify
+            // calls: 298 us at S = 4, 289 us at S = 1).
             S = clamp64((U + 63) / 64, s_min, 8);
+            if (std::min<int64_t>(R, kMfmaRows / 2) * D * S * 4 > kFusedMaxPartialBytes) S = s_min;
+        }
         else
             // While the launch leaves CUs idle, split long key ranges further, down to
             // 256 keys (four tiles) per split: a shorter chain per workgroup for the

@@ -176,8 +176,10 @@ def test_sixteen_row_chunks_only_while_the_grid_fits_the_cus():
     # 48 units x 1 split, four times over (two 16-row chunks, two column halves each), is
     # 192 <= 256 workgroups: 16-row chunks
     assert sw.swattn_plan(desc(), 8, 188).rows_per_chunk == 16
-    # one layer (2 units, 4 splits of one tile): 32 workgroups
+    # one layer (2 units, no split): 8 workgroups; with 4 splits forced, 32
     p = sw.swattn_plan(desc(batch=1), 8, 188)
+    assert p.rows_per_chunk == 16 and p.num_splits == 1 and p.grid == 8
+    p = sw.swattn_plan(desc(batch=1, num_splits=4), 8, 188)
     assert p.rows_per_chunk == 16 and p.num_splits == 4 and p.grid == 32
     # 96 units (48 problems) four times over is 384 > 256: 32-row chunks
     p = sw.swattn_plan(desc(batch=48), 8, 188)
@@ -196,13 +198,18 @@ def test_sixteen_row_chunks_only_while_the_grid_fits_the_cus():
 
 
 def test_small_launches_split_per_tile():
-    # one layer of the verify step: 2 units, 195 keys -> one split per 64-key tile
+    # one layer of plain decode: 2 units, 191 keys -> one split per 64-key tile, whose
+    # partials (4 rows x 256 x 4 splits x 4 B = 16 KiB) the last workgroup merges
+    p = sw.swattn_plan(desc(batch=1), 1, 188)
+    assert p.variant == sw.SWATTN_VARIANT_MFMA and p.num_splits == 3 and p.fused_merge == 1
+    # one layer of the verify step: 16-row partials of 4 splits (64 KiB) would need the
+    # merge kernel -> no split
     p = sw.swattn_plan(desc(batch=1), 8, 188)
-    assert p.variant == sw.SWATTN_VARIANT_MFMA and p.num_splits == 4 and p.merge_grid > 0
+    assert p.variant == sw.SWATTN_VARIANT_MFMA and p.num_splits == 1 and p.merge_grid == 0
     # 24 layers stacked: 48 units, no split
     assert sw.swattn_plan(desc(batch=24), 8, 188).num_splits == 1
     # a forced split count still wins
-    assert sw.swattn_plan(desc(batch=1, num_splits=1), 8, 188).num_splits == 1
+    assert sw.swattn_plan(desc(batch=1, num_splits=4), 8, 188).num_splits == 4
 
 
 def test_long_ranges_split_while_cus_idle():
