@@ -238,6 +238,33 @@ swattn_status_t swattn_append_kv(const swattn_desc_t* desc, const void* k_new, c
                                  void* stream);
 
 /*
+ * swattn_append_verify — swattn_append_kv of the step's n_q new rows, then
+ * swattn_verify, as one call.
+ *
+ * Source: "The Fast Gemma Challenge: our verified-SOTA recipe, in full" (dev.to,
+ * VIDRAFT), full manifest.json — SPECULATIVE_CONFIG (the verify step's target and
+ * drafts bring their own K/V rows, which their attention must already see) and
+ * SPLITKV_VERIFY; section "What each piece does, and why".
+ *
+ * Arguments as in swattn_append_kv (k_new, v_new, new_dtype, with n_new = n_q) and
+ * swattn_verify (the rest); k_cache and v_cache are written.  The result, outputs and
+ * cache bytes, is that of the two calls in order.  Where the plan runs the
+ * matrix-core kernel and both the new rows and the cache are bfloat16 (the append is
+ * then a copy), it is one launch: keys at the new positions are read from k_new /
+ * v_new, and the kernel writes those rows into the cache; otherwise the append
+ * kernel runs first.  In the one-launch form the blocks holding a sequence's new
+ * positions must not lie in another sequence's window (blocks are not shared with
+ * a sequence that is being appended to).  Errors of either call return before
+ * anything is enqueued; no allocation or synchronisation, capturable into a HIP
+ * graph.
+ */
+swattn_status_t swattn_append_verify(const swattn_desc_t* desc, const void* q, const void* k_new, const void* v_new,
+                                     swattn_dtype_t new_dtype, void* k_cache, void* v_cache,
+                                     const int32_t* block_table, const int32_t* ctx_len, int32_t n_q,
+                                     int32_t window, float scale, void* out, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
+/*
  * swattn_greedy_accept — greedy acceptance of one verify step's drafts.
  *
  * Source: "The Fast Gemma Challenge: our verified-SOTA recipe, in full" (dev.to,

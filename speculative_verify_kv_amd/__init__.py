@@ -4,7 +4,7 @@ Argument marshalling only: every step of the computation runs in the HIP
 kernels of ``libswattn.so``.  The functions mirror the C ABI in
 ``include/swattn.h`` one for one (``swattn_plan``, ``swattn_workspace_bytes``,
 ``swattn_workspace_init``, ``swattn_verify``, ``swattn_prefill_plan``, ``swattn_prefill``,
-``swattn_append_kv``, ``swattn_greedy_accept_workspace``,
+``swattn_append_kv``, ``swattn_append_verify``, ``swattn_greedy_accept_workspace``,
 ``swattn_greedy_accept``, ``swattn_check_inputs``, ``swattn_status_str``,
 ``swattn_abi_version``);
 ``verify`` and ``prefill`` are conveniences that fill the descriptor from torch
@@ -33,7 +33,7 @@ STATUS = {
 
 # Symbols declared in include/swattn.h.
 EXPORTED = ("swattn_plan", "swattn_workspace_bytes", "swattn_workspace_init", "swattn_verify", "swattn_prefill_plan",
-            "swattn_prefill", "swattn_append_kv", "swattn_greedy_accept_workspace",
+            "swattn_prefill", "swattn_append_kv", "swattn_append_verify", "swattn_greedy_accept_workspace",
             "swattn_greedy_accept", "swattn_check_inputs", "swattn_status_str", "swattn_abi_version")
 
 
@@ -105,6 +105,11 @@ def lib():
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
                                        ctypes.c_void_p, ctypes.c_void_p]
         L.swattn_append_kv.restype = ctypes.c_int
+        L.swattn_append_verify.argtypes = [P(swattn_desc_t), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
+                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        L.swattn_append_verify.restype = ctypes.c_int
         L.swattn_greedy_accept_workspace.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                                      P(ctypes.c_size_t)]
         L.swattn_greedy_accept_workspace.restype = ctypes.c_int
@@ -199,6 +204,17 @@ def swattn_append_kv(desc, k_new, v_new, new_dtype, block_table, ctx_len, n_new,
                                 _ptr(stream))
     if check and st != 0:
         raise SwattnError(st, "swattn_append_kv")
+    return st
+
+
+def swattn_append_verify(desc, q, k_new, v_new, new_dtype, k_cache, v_cache, block_table, ctx_len, n_q, window,
+                         scale, out, workspace=None, workspace_bytes=0, stream=None, check=True):
+    st = lib().swattn_append_verify(ctypes.byref(desc), _ptr(q), _ptr(k_new), _ptr(v_new), int(new_dtype),
+                                    _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(ctx_len), int(n_q),
+                                    int(window), float(scale), _ptr(out), _ptr(workspace), int(workspace_bytes),
+                                    _ptr(stream))
+    if check and st != 0:
+        raise SwattnError(st, "swattn_append_verify")
     return st
 
 

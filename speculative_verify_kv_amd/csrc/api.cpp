@@ -26,12 +26,19 @@ int dtype_bytes(int dt) { return dt == SWATTN_F32 ? 4 : (dt == SWATTN_BF16 ? 2 :
 namespace swattn {
 namespace {
 
-// One attention call (verify or prefill: they differ only in the n_q cap).
-swattn_status_t attend(const swattn_desc_t* d, const void* q, const void* k_cache, const void* v_cache,
-                       const int32_t* block_table, const int32_t* ctx_len, int32_t n_q, int32_t window,
-                       float scale, void* out, void* workspace, size_t workspace_bytes, void* stream,
-                       int32_t max_nq) {
+// An attention call, checked and laid out (verify or prefill: they differ only in the
+// n_q cap); nothing is enqueued.
+struct AttendCall {
     swattn_plan_t plan;
+    PartitionParams p;
+    MergeParams m;
+};
+
+swattn_status_t prepare_attend(const swattn_desc_t* d, const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* block_table, const int32_t* ctx_len, int32_t n_q, int32_t window,
+                               float scale, void* out, void* workspace, size_t workspace_bytes, int32_t max_nq,
+                               AttendCall* call) {
+    swattn_plan_t& plan = call->plan;
     swattn_status_t st = make_plan(d, n_q, window, max_nq, &plan);
     if (st != SWATTN_OK) return st;
     if (!q || !k_cache || !v_cache || !block_table || !ctx_len || !out) return SWATTN_ERR_NULL;
@@ -66,7 +73,7 @@ swattn_status_t attend(const swattn_desc_t* d, const void* q, const void* k_cach
         ws_lse = reinterpret_cast<float*>(base + SWATTN_WORKSPACE_COUNTER_BYTES + o_bytes);
     }
 
-    PartitionParams p;
+    PartitionParams& p = call->p;
     p.q = q;
     p.k = k_cache;
     p.v = v_cache;
@@ -78,6 +85,8 @@ swattn_status_t attend(const swattn_desc_t* d, const void* q, const void* k_cach
     p.ws_o = ws_o;
     p.ws_lse = ws_lse;
     p.counters = counters;
+    p.k_new = nullptr;
+    p.v_new = nullptr;
     p.B = d->batch;
     p.H = d->num_heads;
     p.Hkv = d->num_kv_heads;
@@ -112,11 +121,8 @@ swattn_status_t attend(const swattn_desc_t* d, const void* q, const void* k_cach
                        plan.rows_per_chunk == kMfmaRows) ? 32 : 64;
     }
 
-    int err = plan.variant == SWATTN_VARIANT_MFMA ? launch_partition_mfma(p, plan.grid, stream)
-                                                  : launch_partition_valu(p, plan.grid, stream);
-    if (err != 0) return SWATTN_ERR_HIP;
-    if (plan.merge_grid > 0) {
-        MergeParams m;
+    MergeParams& m = call->m;
+    {
         m.ws_o = ws_o;
         m.ws_lse = ws_lse;
         m.out = out;
@@ -129,9 +135,76 @@ swattn_status_t attend(const swattn_desc_t* d, const void* q, const void* k_cach
         m.R = (int32_t)R;
         m.S = plan.num_splits;
         m.out_dtype = d->out_dtype;
-        err = launch_merge(m, plan.merge_grid, stream);
-        if (err != 0) return SWATTN_ERR_HIP;
     }
+    return SWATTN_OK;
+}
+
+swattn_status_t launch_attend(const AttendCall& call, void* stream) {
+    const int err = call.plan.variant == SWATTN_VARIANT_MFMA ? launch_partition_mfma(call.p, call.plan.grid, stream)
+                                                             : launch_partition_valu(call.p, call.plan.grid, stream);
+    if (err != 0) return SWATTN_ERR_HIP;
+    if (call.plan.merge_grid > 0 && launch_merge(call.m, call.plan.merge_grid, stream) != 0) return SWATTN_ERR_HIP;
+    return SWATTN_OK;
+}
+
+swattn_status_t attend(const swattn_desc_t* d, const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_table, const int32_t* ctx_len, int32_t n_q, int32_t window,
+                       float scale, void* out, void* workspace, size_t workspace_bytes, void* stream,
+                       int32_t max_nq) {
+    AttendCall call;
+    const swattn_status_t st = prepare_attend(d, q, k_cache, v_cache, block_table, ctx_len, n_q, window, scale,
+                                              out, workspace, workspace_bytes, max_nq, &call);
+    return st != SWATTN_OK ? st : launch_attend(call, stream);
+}
+
+// The checks and launch shape of an append call; nothing is enqueued.
+swattn_status_t prepare_append(const swattn_desc_t* d, const void* k_new, const void* v_new,
+                               swattn_dtype_t new_dtype, const int32_t* block_table, const int32_t* ctx_len,
+                               int32_t n_new, void* k_cache, void* v_cache, AppendParams* out, int64_t* grid_out) {
+    if (!d) return SWATTN_ERR_NULL;
+    if (d->batch < 1 || d->num_kv_heads < 1) return SWATTN_ERR_SHAPE;
+    if (d->head_dim != 64 && d->head_dim != 128 && d->head_dim != 256) return SWATTN_ERR_SHAPE;
+    if (d->block_size < 1 || d->max_blocks_per_seq < 1 || d->num_blocks < 1 || d->max_ctx_len < 1)
+        return SWATTN_ERR_SHAPE;
+    if ((int64_t)d->max_ctx_len > (int64_t)d->max_blocks_per_seq * d->block_size) return SWATTN_ERR_SHAPE;
+    if ((int64_t)d->num_blocks * d->num_kv_heads * d->block_size > INT32_MAX) return SWATTN_ERR_SHAPE;
+    if ((int64_t)d->max_blocks_per_seq * d->block_size > INT32_MAX) return SWATTN_ERR_SHAPE;
+    if (n_new < 1 || n_new > SWATTN_MAX_PREFILL_NQ) return SWATTN_ERR_NQ;
+    if (new_dtype != SWATTN_F32 && new_dtype != SWATTN_BF16) return SWATTN_ERR_DTYPE;
+    if (d->kv_dtype != SWATTN_F32 && d->kv_dtype != SWATTN_BF16 && d->kv_dtype != SWATTN_FP8_E4M3)
+        return SWATTN_ERR_DTYPE;
+    const bool fp8 = d->kv_dtype == SWATTN_FP8_E4M3;
+    if (fp8 && (!d->k_scale || !d->v_scale)) return SWATTN_ERR_DTYPE;
+    if (!fp8 && (d->k_scale || d->v_scale)) return SWATTN_ERR_DTYPE;
+    if (!k_new || !v_new || !block_table || !ctx_len || !k_cache || !v_cache) return SWATTN_ERR_NULL;
+    if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+        !aligned(block_table, 4) || !aligned(ctx_len, 4))
+        return SWATTN_ERR_ALIGN;
+    if (fp8 && (!aligned(d->k_scale, 4) || !aligned(d->v_scale, 4))) return SWATTN_ERR_ALIGN;
+    const int64_t threads = 2 * (int64_t)d->batch * n_new * d->num_kv_heads * (d->head_dim / 8);
+    const int64_t grid = (threads + kBlockThreads - 1) / kBlockThreads;
+    if (grid > INT32_MAX) return SWATTN_ERR_SHAPE;
+
+    AppendParams& p = *out;
+    p.k_new = k_new;
+    p.v_new = v_new;
+    p.k_cache = k_cache;
+    p.v_cache = v_cache;
+    p.block_table = block_table;
+    p.ctx_len = ctx_len;
+    p.k_scale = d->k_scale;
+    p.v_scale = d->v_scale;
+    p.B = d->batch;
+    p.Hkv = d->num_kv_heads;
+    p.D = d->head_dim;
+    p.bs = d->block_size;
+    p.max_blocks = d->max_blocks_per_seq;
+    p.num_blocks = d->num_blocks;
+    p.max_ctx = d->max_ctx_len;
+    p.n_new = n_new;
+    p.new_dtype = new_dtype;
+    p.kv_dtype = d->kv_dtype;
+    *grid_out = grid;
     return SWATTN_OK;
 }
 
@@ -188,50 +261,40 @@ extern "C" swattn_status_t swattn_append_kv(const swattn_desc_t* d, const void* 
                                             const int32_t* ctx_len, int32_t n_new, void* k_cache, void* v_cache,
                                             void* stream) {
     using namespace swattn;
-    if (!d) return SWATTN_ERR_NULL;
-    if (d->batch < 1 || d->num_kv_heads < 1) return SWATTN_ERR_SHAPE;
-    if (d->head_dim != 64 && d->head_dim != 128 && d->head_dim != 256) return SWATTN_ERR_SHAPE;
-    if (d->block_size < 1 || d->max_blocks_per_seq < 1 || d->num_blocks < 1 || d->max_ctx_len < 1)
-        return SWATTN_ERR_SHAPE;
-    if ((int64_t)d->max_ctx_len > (int64_t)d->max_blocks_per_seq * d->block_size) return SWATTN_ERR_SHAPE;
-    if ((int64_t)d->num_blocks * d->num_kv_heads * d->block_size > INT32_MAX) return SWATTN_ERR_SHAPE;
-    if ((int64_t)d->max_blocks_per_seq * d->block_size > INT32_MAX) return SWATTN_ERR_SHAPE;
-    if (n_new < 1 || n_new > SWATTN_MAX_PREFILL_NQ) return SWATTN_ERR_NQ;
-    if (new_dtype != SWATTN_F32 && new_dtype != SWATTN_BF16) return SWATTN_ERR_DTYPE;
-    if (d->kv_dtype != SWATTN_F32 && d->kv_dtype != SWATTN_BF16 && d->kv_dtype != SWATTN_FP8_E4M3)
-        return SWATTN_ERR_DTYPE;
-    const bool fp8 = d->kv_dtype == SWATTN_FP8_E4M3;
-    if (fp8 && (!d->k_scale || !d->v_scale)) return SWATTN_ERR_DTYPE;
-    if (!fp8 && (d->k_scale || d->v_scale)) return SWATTN_ERR_DTYPE;
-    if (!k_new || !v_new || !block_table || !ctx_len || !k_cache || !v_cache) return SWATTN_ERR_NULL;
-    if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
-        !aligned(block_table, 4) || !aligned(ctx_len, 4))
-        return SWATTN_ERR_ALIGN;
-    if (fp8 && (!aligned(d->k_scale, 4) || !aligned(d->v_scale, 4))) return SWATTN_ERR_ALIGN;
-    const int64_t threads = 2 * (int64_t)d->batch * n_new * d->num_kv_heads * (d->head_dim / 8);
-    const int64_t grid = (threads + kBlockThreads - 1) / kBlockThreads;
-    if (grid > INT32_MAX) return SWATTN_ERR_SHAPE;
-
     AppendParams p;
-    p.k_new = k_new;
-    p.v_new = v_new;
-    p.k_cache = k_cache;
-    p.v_cache = v_cache;
-    p.block_table = block_table;
-    p.ctx_len = ctx_len;
-    p.k_scale = d->k_scale;
-    p.v_scale = d->v_scale;
-    p.B = d->batch;
-    p.Hkv = d->num_kv_heads;
-    p.D = d->head_dim;
-    p.bs = d->block_size;
-    p.max_blocks = d->max_blocks_per_seq;
-    p.num_blocks = d->num_blocks;
-    p.max_ctx = d->max_ctx_len;
-    p.n_new = n_new;
-    p.new_dtype = new_dtype;
-    p.kv_dtype = d->kv_dtype;
+    int64_t grid = 0;
+    const swattn_status_t st =
+        prepare_append(d, k_new, v_new, new_dtype, block_table, ctx_len, n_new, k_cache, v_cache, &p, &grid);
+    if (st != SWATTN_OK) return st;
     return launch_kv_append(p, (int)grid, stream) == 0 ? SWATTN_OK : SWATTN_ERR_HIP;
+}
+
+extern "C" swattn_status_t swattn_append_verify(const swattn_desc_t* d, const void* q, const void* k_new,
+                                                const void* v_new, swattn_dtype_t new_dtype, void* k_cache,
+                                                void* v_cache, const int32_t* block_table, const int32_t* ctx_len,
+                                                int32_t n_q, int32_t window, float scale, void* out,
+                                                void* workspace, size_t workspace_bytes, void* stream) {
+    using namespace swattn;
+    AppendParams ap;
+    int64_t agrid = 0;
+    swattn_status_t st =
+        prepare_append(d, k_new, v_new, new_dtype, block_table, ctx_len, n_q, k_cache, v_cache, &ap, &agrid);
+    if (st != SWATTN_OK) return st;
+    AttendCall call;
+    st = prepare_attend(d, q, k_cache, v_cache, block_table, ctx_len, n_q, window, scale, out, workspace,
+                        workspace_bytes, SWATTN_MAX_NQ, &call);
+    if (st != SWATTN_OK) return st;
+    // One launch where the matrix-core kernel can take the new rows as they are (bfloat16
+    // rows into a bfloat16 cache: the append is a copy): it reads the keys at the new
+    // positions from k_new / v_new and writes them into the cache itself.  Otherwise
+    // the append kernel, then the attention call.
+    if (call.plan.variant == SWATTN_VARIANT_MFMA && new_dtype == SWATTN_BF16 && d->kv_dtype == SWATTN_BF16) {
+        call.p.k_new = k_new;
+        call.p.v_new = v_new;
+        return launch_attend(call, stream);
+    }
+    if (launch_kv_append(ap, (int)agrid, stream) != 0) return SWATTN_ERR_HIP;
+    return launch_attend(call, stream);
 }
 
 namespace swattn {

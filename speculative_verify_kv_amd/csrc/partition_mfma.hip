@@ -296,6 +296,11 @@ __global__ __launch_bounds__((Geo<D, FP8, KT, RB>::kNT), (Geo<D, FP8, KT, RB>::k
                     const int64_t rowb = ((int64_t)(phys * p.Hkv + g) * p.bs + off) * G::kRowB;
                     kp = kbase + rowb;
                     vp = vbase + rowb;
+                    if (p.k_new != nullptr && j >= pos0) {   // a new row: from the caller's buffer
+                        const int64_t nrow = (((int64_t)b * p.n_q + (j - pos0)) * p.Hkv + g) * G::kRowB;
+                        kp = reinterpret_cast<const unsigned char*>(p.k_new) + nrow;
+                        vp = reinterpret_cast<const unsigned char*>(p.v_new) + nrow;
+                    }
                 } else {
                     kp = nrow;
                 }
@@ -652,6 +657,29 @@ __global__ __launch_bounds__((Geo<D, FP8, KT, RB>::kNT), (Geo<D, FP8, KT, RB>::k
     if (p.S > 1 && cs == 0 && kh == 0 && dh == 0 && q4 == 0)
         store_partial1(p, p.ws_lse + prow, (l_all == 0.0f ? -INFINITY : m_all + log2f(l_all)) + poison);
     }
+    }
+
+    // ---- fused append: one workgroup per (problem, KV head) copies the n_q new K and V
+    //      rows into the cache (no workgroup of this launch reads those cache rows: the
+    //      keys at the new positions come from k_new / v_new).  Sequences and blocks
+    //      outside the valid range are not written, as by the append call.
+    if (p.k_new != nullptr && rc == 0 && cs == 0 && s == 0 && seq_ok) {
+        const int per = p.n_q * G::kCpr;                  // 16-byte pieces of one tensor's rows
+        for (int idx = tid; idx < 2 * per; idx += NT) {
+            const bool is_v = idx >= per;
+            const int r = is_v ? idx - per : idx;
+            const int i = r / G::kCpr, c = r - i * G::kCpr;
+            const int j = pos0 + i;
+            const int blk = p.bs_log2 >= 0 ? j >> p.bs_log2 : j / p.bs;
+            const int off = j - blk * p.bs;
+            const int phys = p.block_table[(int64_t)b * p.max_blocks + blk];
+            if (phys < 0 || phys >= p.num_blocks) continue;
+            const int64_t src = (((int64_t)b * p.n_q + i) * p.Hkv + g) * G::kRowB + c * 16;
+            const int64_t dst = ((int64_t)(phys * p.Hkv + g) * p.bs + off) * G::kRowB + c * 16;
+            const uint4 w = *reinterpret_cast<const uint4*>(
+                reinterpret_cast<const unsigned char*>(is_v ? p.v_new : p.k_new) + src);
+            *reinterpret_cast<uint4*>(reinterpret_cast<unsigned char*>(const_cast<void*>(is_v ? p.v : p.k)) + dst) = w;
+        }
     }
 
     // ---- split launches: the last workgroup of the row chunk combines the partials

@@ -36,6 +36,11 @@ struct PartitionParams {
     float* ws_o;          // [B*Hkv][S][R][D] normalised partial outputs (S > 1)
     float* ws_lse;        // [B*Hkv][S][R] log2-sum-exp of each partial (S > 1)
     int32_t* counters;    // [B*Hkv][row_chunks] arrivals (fused merge), else NULL
+    // Fused append (matrix-core kernel, bfloat16 rows and cache): the n_q new rows
+    // [B][n_q][Hkv][D] of every sequence, read for the keys at the new positions and
+    // written into the cache; NULL otherwise.
+    const void* k_new;
+    const void* v_new;
     int32_t B, H, Hkv, G, D, bs, max_blocks, num_blocks;
     int32_t bs_log2;      // log2(bs) when bs is a power of two, else -1
     int32_t n_q, window, R, max_ctx;
