@@ -543,13 +543,14 @@ def run_accept(args, torch, np, sw, dev):
 
 def run_layer_graph(args, torch, np, sw, synth, dev):
     """One decode step of the verify workload's 24 layers as a model runs it: per layer,
-    swattn_append_kv of the layer's 8 new K/V rows then swattn_verify of that layer
-    alone (B = 1), and at the end swattn_greedy_accept on the step's logits (8 x
+    swattn_append_verify of that layer alone (B = 1: its 8 new K/V rows appended and its
+    verify, one launch), and at the end swattn_greedy_accept on the step's logits (8 x
     --vocab bf16).  The step is captured into one HIP graph per buffer slot (3 slots,
     graphs replayed round-robin, 20 warm-up replays each, after the manifest's
     LOOPGRAPH_PINGPONG_SLOTS / LOOPGRAPH_WARMUP_CALLS), and compared with the same step
-    issued as three stacked calls (all layers in one append and one verify call).
-    Outputs of both forms must be equal bit for bit."""
+    with separate swattn_append_kv and swattn_verify calls per layer, and issued as
+    three stacked calls (all layers in one append and one verify call).  Outputs of all
+    forms must be equal bit for bit."""
     import oracle
     w = synth.named_workload("verify")
     L, n, H, Hkv, D = w.B, w.n_q, w.H, w.Hkv, w.D
@@ -572,7 +573,7 @@ def run_layer_graph(args, torch, np, sw, synth, dev):
             vn=bf16_dev(rng.standard_normal((L, n, Hkv, D)).astype(np.float32)),
             logits=bf16_dev(rng.standard_normal((1, n, vocab)).astype(np.float32)),
             drafts=torch.from_numpy(rng.integers(0, vocab, (1, n - 1)).astype(np.int32)).to(dev))
-        for form in ("layers", "stacked"):
+        for form in ("fused", "layers", "stacked"):
             slot[form] = dict(out=torch.empty((L, n, H, D), dtype=torch.bfloat16, device=dev),
                               tgt=torch.empty((1, n), dtype=torch.int32, device=dev),
                               acc=torch.empty((1,), dtype=torch.int32, device=dev),
@@ -590,7 +591,12 @@ def run_layer_graph(args, torch, np, sw, synth, dev):
 
     def step(slot, form, cs):
         o = slot[form]
-        if form == "layers":
+        if form == "fused":
+            for l in range(L):
+                sw.swattn_append_verify(desc_l[l], slot["q"][l:l + 1], slot["kn"][l:l + 1], slot["vn"][l:l + 1],
+                                        sw.SWATTN_BF16, k, v, bt[l:l + 1], ctx[l:l + 1], n, w.window, w.scale,
+                                        o["out"][l:l + 1], ws_l, plan_l.workspace_bytes, cs)
+        elif form == "layers":
             for l in range(L):
                 sw.swattn_append_kv(desc_l[l], slot["kn"][l:l + 1], slot["vn"][l:l + 1], sw.SWATTN_BF16,
                                     bt[l:l + 1], ctx[l:l + 1], n, k, v, cs)
@@ -604,7 +610,7 @@ def run_layer_graph(args, torch, np, sw, synth, dev):
 
     stream = torch.cuda.current_stream(dev)
     graphs = {}
-    for form in ("layers", "stacked"):
+    for form in ("fused", "layers", "stacked"):
         graphs[form] = []
         for slot in slots:
             g = torch.cuda.CUDAGraph()
@@ -616,6 +622,8 @@ def run_layer_graph(args, torch, np, sw, synth, dev):
             for g in graphs[form]:
                 g.replay()
     torch.cuda.synchronize()
+    same_fused = all(torch.equal(sl["fused"][key], sl["layers"][key]) for sl in slots
+                     for key in ("out", "tgt", "acc", "nxt"))
     if plan_l.num_splits == plan_all.num_splits:
         same = all(torch.equal(sl["layers"][key], sl["stacked"][key]) for sl in slots
                    for key in ("out", "tgt", "acc", "nxt"))
@@ -646,7 +654,7 @@ def run_layer_graph(args, torch, np, sw, synth, dev):
             torch.cuda.synchronize()
             cold.append(ev0.elapsed_time(ev1) * 1e3)
         res[form] = {"warm_us_per_step": round(warm, 3), "cold_us_per_step": round(statistics.median(cold), 3)}
-    value = res["layers"]["cold_us_per_step"]
+    value = res["fused"]["cold_us_per_step"]
     line = {
         "metric": "decode-step us (24 per-layer KV appends + verify calls + greedy acceptance, one HIP graph)",
         "value": value, "unit": "us/step", "n_gpus": 1, "steps": max(args.steps // 4, 9), "warmup": 20,
@@ -656,11 +664,14 @@ def run_layer_graph(args, torch, np, sw, synth, dev):
                                f"acceptance over 8 x {vocab} bf16 logits; 3 graph slots",
                    "global_batch": 1, "seq_len": max_ctx, "parallelism": "none (1 GPU)"},
         "roofline": None,
-        "timing": {"per_layer_graph": res["layers"], "stacked_graph": res["stacked"],
+        "timing": {"per_layer_graph": res["fused"], "per_layer_graph_separate_append": res["layers"],
+                   "stacked_graph": res["stacked"],
                    "note": "cold = HIP events around one graph replay after a 512 MiB overwrite and read (includes "
                            "the graph launch); warm = graphs replayed back to back, round-robin over the slots"},
         "plan_per_layer": plan_l.as_dict(), "plan_stacked": plan_all.as_dict(),
-        "parity_check": {"ok": bool(same), "what": "per-layer graph == stacked graph, outputs bit for bit"},
+        "parity_check": {"ok": bool(same and same_fused),
+                         "what": "per-layer graph (append_verify) == per-layer graph (append_kv + verify) == "
+                                 "stacked graph, outputs bit for bit"},
         "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)
