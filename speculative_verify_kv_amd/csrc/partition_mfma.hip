@@ -296,7 +296,8 @@ __global__ __launch_bounds__((Geo<D, FP8, KT, RB>::kNT), (Geo<D, FP8, KT, RB>::k
                     const int64_t rowb = ((int64_t)(phys * p.Hkv + g) * p.bs + off) * G::kRowB;
                     kp = kbase + rowb;
                     vp = vbase + rowb;
-                    if (p.k_new != nullptr && j >= pos0) {   // a new row: from the caller's buffer
+                    // a new row (fused append, bfloat16 only): from the caller's buffer
+                    if (!FP8 && p.k_new != nullptr && j >= pos0) {
                         const int64_t nrow = (((int64_t)b * p.n_q + (j - pos0)) * p.Hkv + g) * G::kRowB;
                         kp = reinterpret_cast<const unsigned char*>(p.k_new) + nrow;
                         vp = reinterpret_cast<const unsigned char*>(p.v_new) + nrow;
@@ -663,7 +664,7 @@ __global__ __launch_bounds__((Geo<D, FP8, KT, RB>::kNT), (Geo<D, FP8, KT, RB>::k
     //      rows into the cache (no workgroup of this launch reads those cache rows: the
     //      keys at the new positions come from k_new / v_new).  Sequences and blocks
     //      outside the valid range are not written, as by the append call.
-    if (p.k_new != nullptr && rc == 0 && cs == 0 && s == 0 && seq_ok) {
+    if (!FP8 && p.k_new != nullptr && rc == 0 && cs == 0 && s == 0 && seq_ok) {
         const int per = p.n_q * G::kCpr;                  // 16-byte pieces of one tensor's rows
         for (int idx = tid; idx < 2 * per; idx += NT) {
             const bool is_v = idx >= per;
