@@ -87,6 +87,8 @@ swattn_status_t prepare_attend(const swattn_desc_t* d, const void* q, const void
     p.counters = counters;
     p.k_new = nullptr;
     p.v_new = nullptr;
+    p.k_dst = nullptr;
+    p.v_dst = nullptr;
     p.B = d->batch;
     p.H = d->num_heads;
     p.Hkv = d->num_kv_heads;
@@ -291,6 +293,8 @@ extern "C" swattn_status_t swattn_append_verify(const swattn_desc_t* d, const vo
     if (call.plan.variant == SWATTN_VARIANT_MFMA && new_dtype == SWATTN_BF16 && d->kv_dtype == SWATTN_BF16) {
         call.p.k_new = k_new;
         call.p.v_new = v_new;
+        call.p.k_dst = k_cache;
+        call.p.v_dst = v_cache;
         return launch_attend(call, stream);
     }
     if (launch_kv_append(ap, (int)agrid, stream) != 0) return SWATTN_ERR_HIP;

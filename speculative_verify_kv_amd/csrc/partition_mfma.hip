@@ -679,7 +679,7 @@ __global__ __launch_bounds__((Geo<D, FP8, KT, RB>::kNT), (Geo<D, FP8, KT, RB>::k
             const int64_t dst = ((int64_t)(phys * p.Hkv + g) * p.bs + off) * G::kRowB + c * 16;
             const uint4 w = *reinterpret_cast<const uint4*>(
                 reinterpret_cast<const unsigned char*>(is_v ? p.v_new : p.k_new) + src);
-            *reinterpret_cast<uint4*>(reinterpret_cast<unsigned char*>(const_cast<void*>(is_v ? p.v : p.k)) + dst) = w;
+            *reinterpret_cast<uint4*>(reinterpret_cast<unsigned char*>(is_v ? p.v_dst : p.k_dst) + dst) = w;
         }
     }
 

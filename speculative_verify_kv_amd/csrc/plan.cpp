@@ -103,7 +103,9 @@ swattn_status_t make_plan(const swattn_desc_t* d, int32_t n_q, int32_t window, i
             // split costs more than it saves (the 24-layer step of per-layer verify
             // calls: 298 us at S = 4, 289 us at S = 1).
             S = clamp64((U + 63) / 64, s_min, 8);
-            if (std::min<int64_t>(R, kMfmaRows / 2) * D * S * 4 > kFusedMaxPartialBytes) S = s_min;
+            const bool half = kMfmaHalfRows && d->head_dim == 256 && 4 * units * S <= kComputeUnits;
+            const int64_t chunk_rows = std::min<int64_t>(R, half ? kMfmaRows / 2 : kMfmaRows);
+            if (chunk_rows * D * S * 4 > kFusedMaxPartialBytes) S = s_min;
         }
         else
             // While the launch leaves CUs idle, split long key ranges further, down to

@@ -38,9 +38,12 @@ struct PartitionParams {
     int32_t* counters;    // [B*Hkv][row_chunks] arrivals (fused merge), else NULL
     // Fused append (matrix-core kernel, bfloat16 rows and cache): the n_q new rows
     // [B][n_q][Hkv][D] of every sequence, read for the keys at the new positions and
-    // written into the cache; NULL otherwise.
+    // written into the cache through k_dst / v_dst (the same caches as k / v); NULL
+    // otherwise.
     const void* k_new;
     const void* v_new;
+    void* k_dst;
+    void* v_dst;
     int32_t B, H, Hkv, G, D, bs, max_blocks, num_blocks;
     int32_t bs_log2;      // log2(bs) when bs is a power of two, else -1
     int32_t n_q, window, R, max_ctx;

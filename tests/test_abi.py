@@ -208,6 +208,11 @@ def test_small_launches_split_per_tile():
     assert p.variant == sw.SWATTN_VARIANT_MFMA and p.num_splits == 1 and p.merge_grid == 0
     # 24 layers stacked: 48 units, no split
     assert sw.swattn_plan(desc(batch=24), 8, 188).num_splits == 1
+    # head_dim 64 keeps 32-row chunks: 32 rows x 64 x 4 splits x 4 B = 32 KiB -> no split;
+    # its plain decode (4 rows) splits, merged by the last workgroup
+    assert sw.swattn_plan(desc(batch=1, head_dim=64), 8, 188).num_splits == 1
+    p = sw.swattn_plan(desc(batch=1, head_dim=64), 1, 188)
+    assert p.num_splits == 3 and p.fused_merge == 1
     # a forced split count still wins
     assert sw.swattn_plan(desc(batch=1, num_splits=4), 8, 188).num_splits == 4
 
