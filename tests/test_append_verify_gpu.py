@@ -36,6 +36,12 @@ CASES = [
     dict(id="e4m3_cache", B=3, n_q=8, ctx=[4096, 500, 9], kv="e4m3"),
     dict(id="f32_rows", B=3, n_q=8, ctx=[4096, 500, 9], new="f32"),
     dict(id="valu", B=3, n_q=8, ctx=[4096, 500, 9], variant=sw.SWATTN_VARIANT_VALU),
+    # other head sizes, group sizes and block sizes through the one-launch form (the
+    # in-kernel copy follows each row size and block arithmetic)
+    dict(id="d64_mha", B=3, n_q=3, ctx=[700, 40, 3], D=64, H=4, Hkv=4),
+    dict(id="d128_g8", B=2, n_q=5, ctx=[2000, 190], D=128, H=16, Hkv=2),
+    dict(id="bs1", B=2, n_q=8, ctx=[400, 9], bs=1, max_blocks=512),
+    dict(id="bs300", B=2, n_q=8, ctx=[600, 301], bs=300, max_blocks=2, window=100),
 ]
 
 
@@ -48,12 +54,14 @@ def _gpu():
 
 def _inputs(c, seed):
     kv = c.get("kv", "bf16")
-    kw = dict(B=c["B"], H=8, Hkv=2, D=256, n_q=c["n_q"], window=188, bs=16, seed=seed,
-              kv_dtype=synth.workloads.E4M3 if kv == "e4m3" else synth.workloads.BF16, recent=188 + c["n_q"] - 1)
+    window = c.get("window", 188)
+    kw = dict(B=c["B"], H=c.get("H", 8), Hkv=c.get("Hkv", 2), D=c.get("D", 256), n_q=c["n_q"], window=window,
+              bs=c.get("bs", 16), seed=seed, kv_dtype=synth.workloads.E4M3 if kv == "e4m3" else synth.workloads.BF16,
+              recent=window + c["n_q"] - 1)
     if "ctx_range" in c:
         w = synth.make_workload(c["id"], ctx=None, ctx_range=c["ctx_range"], max_blocks=c["max_blocks"], **kw)
     else:
-        w = synth.make_workload(c["id"], ctx=c["ctx"], max_blocks=256, **kw)
+        w = synth.make_workload(c["id"], ctx=c["ctx"], max_blocks=c.get("max_blocks", 256), **kw)
     rng = np.random.default_rng(seed + 100)
     shape = (w.B, w.n_q, w.Hkv, w.D)
     kn = rng.standard_normal(shape).astype(np.float32)
