@@ -108,6 +108,7 @@ __global__ __launch_bounds__(kBlockThreads) void partition_valu_kernel(Partition
     __shared__ __attribute__((aligned(16))) float red[KGR][RC][D];
     __shared__ float rstat[RC][2];
     __shared__ int64_t roff[kValuMaxKeys];    // cache row of key k0 + kk (element offset), or -1
+    __shared__ int tbl[kBlockThreads];        // the problem's block-table row, when it is that short
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -121,6 +122,10 @@ __global__ __launch_bounds__(kBlockThreads) void partition_valu_kernel(Partition
     const int g = lin % p.Hkv;
     const int b = lin / p.Hkv;
 
+    // A block-table row that fits one entry per thread is read while ctx_len is in
+    // flight: one dependent round trip fewer before the first K loads.
+    const bool short_row = p.max_blocks <= kBlockThreads;
+    const int tb = (short_row && tid < p.max_blocks) ? p.block_table[(int64_t)b * p.max_blocks + tid] : 0;
     const int ctx = p.ctx_len[b];
     const bool seq_ok = ctx >= p.n_q && ctx <= p.max_blocks * p.bs && ctx <= p.max_ctx;
     const int pos0 = seq_ok ? ctx - p.n_q : 0;
@@ -143,9 +148,6 @@ __global__ __launch_bounds__(kBlockThreads) void partition_valu_kernel(Partition
         osc = p.v_scale[g];
     }
 
-    // ---- phase 0: cache rows of the split's keys -> LDS --------------------------------
-    for (int kk = tid; kk < nk; kk += kBlockThreads) roff[kk] = valu_row_offset(p, b, g, k0 + kk);
-
     // ---- Q rows of this chunk -> LDS (float) ---------------------------------------
     for (int idx = tid; idx < RC * D; idx += kBlockThreads) {
         const int rr = idx / D, d = idx - rr * D;
@@ -159,6 +161,21 @@ __global__ __launch_bounds__(kBlockThreads) void partition_valu_kernel(Partition
                                           : bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(p.q)[qi]);
         }
         qs[rr][d] = val;
+    }
+    if (short_row) tbl[tid] = tb;
+    __syncthreads();
+
+    // ---- phase 0: cache rows of the split's keys -> LDS --------------------------------
+    for (int kk = tid; kk < nk; kk += kBlockThreads) {
+        const int j = k0 + kk;
+        if (short_row) {
+            const int blk = j / p.bs;
+            const int phys = tbl[blk];
+            roff[kk] = (phys < 0 || phys >= p.num_blocks) ? -1
+                                                          : (((int64_t)phys * p.Hkv + g) * p.bs + (j - blk * p.bs)) * (int64_t)p.D;
+        } else {
+            roff[kk] = valu_row_offset(p, b, g, j);
+        }
     }
     __syncthreads();
 
