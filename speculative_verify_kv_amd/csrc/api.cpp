@@ -107,6 +107,7 @@ swattn_status_t prepare_attend(const swattn_desc_t* d, const void* q, const void
     p.S = plan.num_splits;
     p.rows_per_chunk = plan.rows_per_chunk;
     p.row_chunks = plan.row_chunks;
+    p.col_splits = (int32_t)((int64_t)plan.grid / ((int64_t)d->batch * d->num_kv_heads * plan.row_chunks * plan.num_splits));
     p.q_dtype = d->q_dtype;
     p.kv_dtype = d->kv_dtype;
     p.out_dtype = d->out_dtype;

@@ -58,7 +58,7 @@ typedef int int2_t __attribute__((ext_vector_type(2)));
 // KT = keys per tile.  64: two key halves of 32, one per wave pair, merged at the
 // end.  32: every wave takes all 32 keys of a tile and the waves split the output
 // columns instead, which halves the LDS a workgroup needs (no merge either).
-template <int D, bool FP8, int KT, int RB = 2>
+template <int D, bool FP8, int KT, int RB = 2, int CS = 1>
 struct Geo {
     static constexpr int kT = KT;
     static constexpr bool kSplitKeys = KT == 64;
@@ -70,9 +70,10 @@ struct Geo {
     static constexpr int kNiK = kT / kRpi;                  // load instructions per K (or V) tile
     static constexpr int kTileB = kT * kRowB;               // bytes of one K tile
     static_assert(kCpr >= 4 && kCpr <= 64 && kNiK * 1024 == kTileB, "tile geometry");
-    // 16-row chunks also split the output columns between two workgroups: each loads
-    // whole K rows (both compute the chunk's scores) and its own half of every V row.
-    static constexpr int kCS = RB == 1 ? 2 : 1;             // column splits
+    // 16-row chunks may also split the output columns between two workgroups: each
+    // loads whole K rows (both compute the chunk's scores) and its own half of every V row.
+    static_assert(CS == 1 || (CS == 2 && RB == 1), "column splits of 16-row chunks only");
+    static constexpr int kCS = CS;                          // column splits
     static constexpr int kRowBV = kRowB / kCS;              // bytes of a V row this workgroup loads
     static constexpr int kCprV = kRowBV / 16;
     static constexpr int kRpiV = 64 / kCprV;
@@ -194,9 +195,9 @@ __device__ __forceinline__ void dma16(const void* src, const void* lds_dst) {
 }
 #pragma clang diagnostic pop
 
-template <int D, bool FP8, bool OUT_F32, int KT, int RB>
-__global__ __launch_bounds__((Geo<D, FP8, KT, RB>::kNT), (Geo<D, FP8, KT, RB>::kBlocks)) void partition_mfma_kernel(PartitionParams p) {
-    using G = Geo<D, FP8, KT, RB>;
+template <int D, bool FP8, bool OUT_F32, int KT, int RB, int CS>
+__global__ __launch_bounds__((Geo<D, FP8, KT, RB, CS>::kNT), (Geo<D, FP8, KT, RB, CS>::kBlocks)) void partition_mfma_kernel(PartitionParams p) {
+    using G = Geo<D, FP8, KT, RB, CS>;
     constexpr int kT = KT;
     constexpr int NT = G::kNT;
     constexpr int KS = D / 32;                   // 32-dim k-steps of S^T = K Q^T
@@ -689,28 +690,28 @@ __global__ __launch_bounds__((Geo<D, FP8, KT, RB>::kNT), (Geo<D, FP8, KT, RB>::k
 
 
 
-template <int D, int KT, bool WITH_FP8, int RB>
+template <int D, int KT, bool WITH_FP8, int RB, int CS = 1>
 int launch_dk(const PartitionParams& p, int grid, hipStream_t st) {
     const bool fp8 = p.kv_dtype == SWATTN_FP8_E4M3;
     const bool of32 = p.out_dtype == SWATTN_F32;
-    const dim3 grd((unsigned)(p.B * p.Hkv), (unsigned)(p.row_chunks * Geo<D, false, KT, RB>::kCS), (unsigned)p.S);
+    const dim3 grd((unsigned)(p.B * p.Hkv), (unsigned)(p.row_chunks * CS), (unsigned)p.S);
     if ((int64_t)grd.x * grd.y * grd.z != grid) return (int)hipErrorInvalidValue;
     if constexpr (WITH_FP8) {
         if (fp8) {
-            const dim3 blk(Geo<D, true, KT, RB>::kNT);
+            const dim3 blk(Geo<D, true, KT, RB, CS>::kNT);
             if (of32)
-                hipLaunchKernelGGL((partition_mfma_kernel<D, true, true, KT, RB>), grd, blk, 0, st, p);
+                hipLaunchKernelGGL((partition_mfma_kernel<D, true, true, KT, RB, CS>), grd, blk, 0, st, p);
             else
-                hipLaunchKernelGGL((partition_mfma_kernel<D, true, false, KT, RB>), grd, blk, 0, st, p);
+                hipLaunchKernelGGL((partition_mfma_kernel<D, true, false, KT, RB, CS>), grd, blk, 0, st, p);
             return (int)hipGetLastError();
         }
     }
     if (fp8) return (int)hipErrorInvalidValue;
-    const dim3 blk(Geo<D, false, KT, RB>::kNT);
+    const dim3 blk(Geo<D, false, KT, RB, CS>::kNT);
     if (of32)
-        hipLaunchKernelGGL((partition_mfma_kernel<D, false, true, KT, RB>), grd, blk, 0, st, p);
+        hipLaunchKernelGGL((partition_mfma_kernel<D, false, true, KT, RB, CS>), grd, blk, 0, st, p);
     else
-        hipLaunchKernelGGL((partition_mfma_kernel<D, false, false, KT, RB>), grd, blk, 0, st, p);
+        hipLaunchKernelGGL((partition_mfma_kernel<D, false, false, KT, RB, CS>), grd, blk, 0, st, p);
     return (int)hipGetLastError();
 }
 
@@ -722,7 +723,8 @@ int launch_d(const PartitionParams& p, int grid, hipStream_t st) {
         if (p.tile_keys == 32 && p.kv_dtype == SWATTN_BF16 && p.rows_per_chunk == 32)
             return launch_dk<D, 32, false, 2>(p, grid, st);
         // 16-row chunks: bfloat16 and E4M3 caches with 64-key tiles
-        if (p.tile_keys == 64 && p.rows_per_chunk == 16) return launch_dk<D, 64, true, 1>(p, grid, st);
+        if (p.tile_keys == 64 && p.rows_per_chunk == 16)
+            return p.col_splits == 2 ? launch_dk<D, 64, true, 1, 2>(p, grid, st) : launch_dk<D, 64, true, 1, 1>(p, grid, st);
     }
     if (p.tile_keys == 64 && p.rows_per_chunk == 32) return launch_dk<D, 64, true, 2>(p, grid, st);
     return (int)hipErrorInvalidValue;

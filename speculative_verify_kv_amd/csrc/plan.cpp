@@ -88,6 +88,7 @@ swattn_status_t make_plan(const swattn_desc_t* d, int32_t n_q, int32_t window, i
     const int64_t U = std::min<int64_t>(d->max_ctx_len, (int64_t)window + qpc - 1);   // keys per chunk
 
     int64_t rows_per_chunk, S;
+    int64_t col_splits = 1;
     if (variant == SWATTN_VARIANT_MFMA) {
         rows_per_chunk = kMfmaRows;
         const int64_t s_min = (U + kMfmaMaxKeys - 1) / kMfmaMaxKeys;
@@ -103,7 +104,7 @@ swattn_status_t make_plan(const swattn_desc_t* d, int32_t n_q, int32_t window, i
             // split costs more than it saves (the 24-layer step of per-layer verify
             // calls: 298 us at S = 4, 289 us at S = 1).
             S = clamp64((U + 63) / 64, s_min, 8);
-            const bool half = kMfmaHalfRows && d->head_dim == 256 && 4 * units * S <= kComputeUnits;
+            const bool half = kMfmaHalfRows && d->head_dim == 256 && 2 * units * S <= kComputeUnits;
             const int64_t chunk_rows = std::min<int64_t>(R, half ? kMfmaRows / 2 : kMfmaRows);
             if (chunk_rows * D * S * 4 > kFusedMaxPartialBytes) S = s_min;
         }
@@ -112,13 +113,17 @@ swattn_status_t make_plan(const swattn_desc_t* d, int32_t n_q, int32_t window, i
             // 256 keys (four tiles) per split: a shorter chain per workgroup for the
             // cost of a merge (full context 1024: 30.7 -> 25.5 us at S = 4).
             S = std::max(s_min, std::min(kComputeUnits / units, (U + 255) / 256));
-        // Head_dim 256 launches that fit the CUs four times over take 16-row chunks, each
-        // split over two workgroups by output columns: four workgroups share a 32-row
-        // chunk's keys (each reading all K rows and its half of every V row), each with a
-        // quarter of the PV work; the outputs stay disjoint, so nothing merges (one verify
-        // step of 24 layers: 32-row chunks 15.0 us, 16-row chunks 12.1 us, split by
-        // columns too 11.2 us; plain decode 12.1 -> 10.4 us).
-        if (kMfmaHalfRows && d->head_dim == 256 && 4 * units * S <= kComputeUnits) rows_per_chunk = kMfmaRows / 2;
+        // Head_dim 256 launches that fit the CUs twice over take 16-row chunks: two
+        // workgroups share a 32-row chunk's keys, each with half the matrix work; four
+        // times over, each 16-row chunk is also split over two workgroups by output
+        // columns (each reading all K rows and its half of every V row).  The outputs stay
+        // disjoint, so nothing merges (one verify step of 24 layers: 32-row chunks
+        // 15.0 us, 16-row chunks 12.1 us, split by columns too 11.2 us; plain decode
+        // 12.1 -> 10.4 us).
+        if (kMfmaHalfRows && d->head_dim == 256 && 2 * units * S <= kComputeUnits) {
+            rows_per_chunk = kMfmaRows / 2;
+            if (4 * units * S <= kComputeUnits) col_splits = 2;
+        }
     } else {
         rows_per_chunk = kValuRowsPerChunk;
         const int64_t row_chunks = (R + rows_per_chunk - 1) / rows_per_chunk;
@@ -131,8 +136,6 @@ swattn_status_t make_plan(const swattn_desc_t* d, int32_t n_q, int32_t window, i
             S = clamp64((kFillTarget + units - 1) / units, s_min, s_cap);
     }
     const int64_t row_chunks = (R + rows_per_chunk - 1) / rows_per_chunk;
-    // 16-row chunks run as two workgroups each (output column halves)
-    const int64_t col_splits = (variant == SWATTN_VARIANT_MFMA && rows_per_chunk == kMfmaRows / 2) ? 2 : 1;
     const int64_t grid = (int64_t)d->batch * d->num_kv_heads * row_chunks * col_splits * S;
     if (grid > INT32_MAX) return SWATTN_ERR_SHAPE;
     // the matrix-core kernel launches a (B * Hkv, row chunks, splits) grid

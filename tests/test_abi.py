@@ -181,9 +181,12 @@ def test_sixteen_row_chunks_only_while_the_grid_fits_the_cus():
     assert p.rows_per_chunk == 16 and p.num_splits == 1 and p.grid == 8
     p = sw.swattn_plan(desc(batch=1, num_splits=4), 8, 188)
     assert p.rows_per_chunk == 16 and p.num_splits == 4 and p.grid == 32
-    # 96 units (48 problems) four times over is 384 > 256: 32-row chunks
+    # 96 units (48 problems): four times over is 384 > 256, twice over 192 -> 16-row chunks
+    # without the column split; 160 units: 32-row chunks
     p = sw.swattn_plan(desc(batch=48), 8, 188)
-    assert p.rows_per_chunk == 32 and p.grid == 48 * 2
+    assert p.rows_per_chunk == 16 and p.grid == 48 * 2 * 2
+    p = sw.swattn_plan(desc(batch=80), 8, 188)
+    assert p.rows_per_chunk == 32 and p.grid == 80 * 2
     # 64 units: 16-row chunks again (256 workgroups)
     p = sw.swattn_plan(desc(batch=32), 8, 188)
     assert p.rows_per_chunk == 16 and p.grid == 256

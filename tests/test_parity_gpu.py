@@ -294,6 +294,30 @@ def test_sixteen_row_chunks(k):
         gu.check(got, ref, w.kv_dtype, True, label=f"sixteen{k} S={S}")
 
 
+# 16-row chunks whose launch fits the CUs twice but not four times over run without
+# the column split: one workgroup per 16-row chunk, all output columns
+SIXTEEN_WHOLE = [
+    dict(B=48, H=8, Hkv=2, n_q=8, window=188, ctx_range=(8, 1500), kv="bf16"),     # 96 units
+    dict(B=40, H=8, Hkv=2, n_q=6, window=60, ctx_range=(6, 900), kv="e4m3"),       # 24 rows: ragged chunk
+]
+
+
+@pytest.mark.parametrize("k", range(len(SIXTEEN_WHOLE)))
+def test_sixteen_row_chunks_whole_columns(k):
+    c = dict(SIXTEEN_WHOLE[k])
+    kv = c.pop("kv")
+    w = synth.make_workload(f"sixteenwhole{k}", D=256, bs=16, seed=90 + k, ctx=None,
+                            kv_dtype=synth.workloads.E4M3 if kv == "e4m3" else synth.workloads.BF16, **c)
+    ref = gu.reference(w)
+    t = gu.upload(w)
+    gu.log(f"[16-row whole] case {k} kv {kv}")
+    for out_f32 in (True, False):
+        got, plan = gu.run(w, t, out_f32=out_f32)
+        assert plan.rows_per_chunk == 16 and plan.num_splits == 1, plan.as_dict()
+        assert plan.grid == w.B * w.Hkv * plan.row_chunks, plan.as_dict()      # no column split
+        gu.check(got, ref, w.kv_dtype, out_f32, label=f"sixteenwhole{k} f32={out_f32}")
+
+
 # ---------------------------------------------------------------------------
 # many rows per KV head and more 32-row chunks than CUs (head_dim 256; 32-key tiles
 # for bfloat16 caches): ragged last chunks (a row block with no row), both cache
