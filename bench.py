@@ -9,8 +9,10 @@ table, seed 1.  Inputs are resident in HBM before timing starts.
 
 Timing: ``--warmup`` untimed calls, then ``--steps`` timed calls captured in
 one HIP graph (the serving loop's way of launching), each preceded by an
-overwrite of 512 MiB so the 256 MB Infinity Cache and the L2s hold nothing of
-the window (cold cache).  The same graph without the calls is timed as well;
+overwrite of 512 MiB and a read of another 512 MiB, so that the 256 MB Infinity
+Cache and the L2s hold nothing of the inputs and no dirty line of the overwrite
+is left to write back during the call (cold cache).  The same graph without the
+calls is timed as well;
 ``value`` is the difference divided by the number of calls (median of 3
 replays), i.e. the cold per-call time as the kernel trace sees it.  Also
 reported: eager calls bracketed one by one with HIP events (adds dispatch
@@ -23,6 +25,8 @@ counter summary committed under profiles/ when it was taken on the current
 kernel source, else null.  ``cpu_baseline``: the float64 oracle on this host.
 
 Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 20]
+       [--workload verify|decode|batched_fp8|batched_bf16|wide_verify|fullctx_*|tiny_decode|prefill_512]
+       [--op attention|append_kv|accept|layer_graph]
 """
 import argparse
 import hashlib
