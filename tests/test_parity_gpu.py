@@ -511,3 +511,19 @@ def test_e4m3_every_code_through_window_one(variant):
         row = got[0, 1, h]
         assert np.array_equal(np.isnan(row), np.isnan(table))
         assert np.array_equal(row[~np.isnan(table)], table[~np.isnan(table)])
+
+
+# ---------------------------------------------------------------------------
+# the API's largest step: 64 queries (and a 512-position prefill chunk) with a window
+# covering the whole 4096-position context, so the key range needs the most splits
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("n_q,prefill", [(64, False), (512, True)])
+def test_largest_queries_full_window(n_q, prefill):
+    w = synth.make_workload(f"largest{n_q}", B=1, H=8, Hkv=2, D=256, n_q=n_q, window=4096, ctx=[4096], bs=16,
+                            seed=110 + n_q % 7, max_blocks=256)
+    ref = gu.reference(w)
+    gu.log(f"[largest] n_q {n_q} window 4096 ctx 4096")
+    got, plan = gu.run(w, out_f32=True, max_ctx=4096, prefill=prefill)
+    gu.log(f"  plan {plan.as_dict()}")
+    assert plan.num_splits >= 8                      # 4096 + n_q - 1 keys, at most 512 per workgroup
+    gu.check(got, ref, w.kv_dtype, True, label=f"largest n_q={n_q}")
