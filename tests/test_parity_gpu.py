@@ -275,6 +275,7 @@ SIXTEEN = [
     dict(B=2, H=8, Hkv=2, n_q=6, window=50, ctx=[6, 1000], kv="e4m3", S=(1, 2)),      # 24 rows: a ragged second chunk
     dict(B=2, H=16, Hkv=2, n_q=3, window=7, ctx=[40, 300], kv="bf16", S=(1, 4)),       # G 8, 24 rows
     dict(B=1, H=4, Hkv=1, n_q=4, window=188, ctx=[188], kv="e4m3", S=(1, 3)),          # exactly 16 rows
+    dict(B=2, H=32, Hkv=2, n_q=3, window=100, ctx=[3, 2000], kv="bf16", S=(1, 2)),      # GQA 16, 48 rows
 ]
 
 
