@@ -70,9 +70,10 @@ struct Geo {
     static constexpr int kNiK = kT / kRpi;                  // load instructions per K (or V) tile
     static constexpr int kTileB = kT * kRowB;               // bytes of one K tile
     static_assert(kCpr >= 4 && kCpr <= 64 && kNiK * 1024 == kTileB, "tile geometry");
-    // 16-row chunks may also split the output columns between two workgroups: each
-    // loads whole K rows (both compute the chunk's scores) and its own half of every V row.
-    static_assert(CS == 1 || (CS == 2 && RB == 1), "column splits of 16-row chunks only");
+    // 16-row chunks may also split the output columns between two or four workgroups:
+    // each loads whole K rows (all compute the chunk's scores) and its own part of every
+    // V row.
+    static_assert(CS == 1 || ((CS == 2 || CS == 4) && RB == 1), "column splits of 16-row chunks only");
     static constexpr int kCS = CS;                          // column splits
     static constexpr int kRowBV = kRowB / kCS;              // bytes of a V row this workgroup loads
     static constexpr int kCprV = kRowBV / 16;
@@ -642,7 +643,15 @@ __global__ __launch_bounds__((Geo<D, FP8, KT, RB, CS>::kNT), (Geo<D, FP8, KT, RB
 #pragma unroll
     for (int db = 0; db < DB / 2; ++db) {
         const f32x4_t other = *reinterpret_cast<const f32x4_t*>(src + db * 16 + q4 * 4);
-        const f32x4_t v = (pick(kh, o[DB / 2 + db], o[db]) * w_me + other * w_o) * inv + poison;
+        const f32x4_t mine = pick(kh, o[DB / 2 + db], o[db]);
+        // key half 0's term first whichever wave finalises the column, so that the
+        // result does not depend on how a launch splits the columns
+        const f32x4_t h0 = pick(kh, other, mine), h1 = pick(kh, mine, other);
+        const float w0 = kh ? w_o : w_me, w1 = kh ? w_me : w_o;
+        f32x4_t num;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) num[e] = __builtin_fmaf(h0[e], w0, h1[e] * w1);
+        const f32x4_t v = num * inv + poison;
         if (p.S == 1) {
             if constexpr (OUT_F32) {
                 *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(p.out) + obase + db * 16) = v;
@@ -724,7 +733,9 @@ int launch_d(const PartitionParams& p, int grid, hipStream_t st) {
             return launch_dk<D, 32, false, 2>(p, grid, st);
         // 16-row chunks: bfloat16 and E4M3 caches with 64-key tiles
         if (p.tile_keys == 64 && p.rows_per_chunk == 16)
-            return p.col_splits == 2 ? launch_dk<D, 64, true, 1, 2>(p, grid, st) : launch_dk<D, 64, true, 1, 1>(p, grid, st);
+            return p.col_splits == 4   ? launch_dk<D, 64, true, 1, 4>(p, grid, st)
+                   : p.col_splits == 2 ? launch_dk<D, 64, true, 1, 2>(p, grid, st)
+                                       : launch_dk<D, 64, true, 1, 1>(p, grid, st);
     }
     if (p.tile_keys == 64 && p.rows_per_chunk == 32) return launch_dk<D, 64, true, 2>(p, grid, st);
     return (int)hipErrorInvalidValue;

@@ -104,7 +104,8 @@ swattn_status_t make_plan(const swattn_desc_t* d, int32_t n_q, int32_t window, i
             // split costs more than it saves (the 24-layer step of per-layer verify
             // calls: 298 us at S = 4, 289 us at S = 1).
             S = clamp64((U + 63) / 64, s_min, 8);
-            const bool half = kMfmaHalfRows && d->head_dim == 256 && 2 * units * S <= kComputeUnits;
+            const bool half = kMfmaHalfRows && d->head_dim == 256 &&
+                              (int64_t)d->batch * d->num_kv_heads * ((R + 15) / 16) * S <= kComputeUnits;
             const int64_t chunk_rows = std::min<int64_t>(R, half ? kMfmaRows / 2 : kMfmaRows);
             if (chunk_rows * D * S * 4 > kFusedMaxPartialBytes) S = s_min;
         }
@@ -113,16 +114,17 @@ swattn_status_t make_plan(const swattn_desc_t* d, int32_t n_q, int32_t window, i
             // 256 keys (four tiles) per split: a shorter chain per workgroup for the
             // cost of a merge (full context 1024: 30.7 -> 25.5 us at S = 4).
             S = std::max(s_min, std::min(kComputeUnits / units, (U + 255) / 256));
-        // Head_dim 256 launches that fit the CUs twice over take 16-row chunks: two
-        // workgroups share a 32-row chunk's keys, each with half the matrix work; four
-        // times over, each 16-row chunk is also split over two workgroups by output
-        // columns (each reading all K rows and its half of every V row).  The outputs stay
-        // disjoint, so nothing merges (one verify step of 24 layers: 32-row chunks
-        // 15.0 us, 16-row chunks 12.1 us, split by columns too 11.2 us; plain decode
-        // 12.1 -> 10.4 us).
-        if (kMfmaHalfRows && d->head_dim == 256 && 2 * units * S <= kComputeUnits) {
+        // Head_dim 256 launches whose 16-row chunks fit the CUs take them: two workgroups
+        // share a 32-row chunk's keys, each with half the matrix work.  Where they fit
+        // twice or four times over, each 16-row chunk is also split over two or four
+        // workgroups by output columns (each reading all K rows and its part of every V
+        // row).  The outputs stay disjoint, so nothing merges (one verify step of 24
+        // layers: 32-row chunks 15.0 us, 16-row chunks 12.1 us, split by columns too
+        // 11.2 us; plain decode 12.1 -> 10.4 us).
+        const int64_t g16 = (int64_t)d->batch * d->num_kv_heads * ((R + 15) / 16) * S;
+        if (kMfmaHalfRows && d->head_dim == 256 && g16 <= kComputeUnits) {
             rows_per_chunk = kMfmaRows / 2;
-            if (4 * units * S <= kComputeUnits) col_splits = 2;
+            col_splits = 4 * g16 <= kComputeUnits ? 4 : (2 * g16 <= kComputeUnits ? 2 : 1);
         }
     } else {
         rows_per_chunk = kValuRowsPerChunk;

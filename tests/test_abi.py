@@ -173,14 +173,22 @@ def test_prefill_plan_caps_and_per_chunk_keys():
 
 
 def test_sixteen_row_chunks_only_while_the_grid_fits_the_cus():
-    # 48 units x 1 split, four times over (two 16-row chunks, two column halves each), is
-    # 192 <= 256 workgroups: 16-row chunks
-    assert sw.swattn_plan(desc(), 8, 188).rows_per_chunk == 16
-    # one layer (2 units, no split): 8 workgroups; with 4 splits forced, 32
+    # the 16-row grid is B x Hkv x ceil(R / 16) x S workgroups; column splits by 2 or 4 where
+    # it fits the CUs 2 or 4 times over.  Verify step: 96 16-row chunks, twice over 192
+    p = sw.swattn_plan(desc(), 8, 188)
+    assert p.rows_per_chunk == 16 and p.grid == 96 * 2
+    # one layer (2 units, no split): 4 16-row chunks, four column quarters each; with 4
+    # splits forced, 16 chunk-splits, four quarters each
     p = sw.swattn_plan(desc(batch=1), 8, 188)
-    assert p.rows_per_chunk == 16 and p.num_splits == 1 and p.grid == 8
+    assert p.rows_per_chunk == 16 and p.num_splits == 1 and p.grid == 4 * 4
     p = sw.swattn_plan(desc(batch=1, num_splits=4), 8, 188)
-    assert p.rows_per_chunk == 16 and p.num_splits == 4 and p.grid == 32
+    assert p.rows_per_chunk == 16 and p.num_splits == 4 and p.grid == 16 * 4
+    # plain decode: one 16-row chunk per KV head.  24 layers: 48, four times over 192;
+    # 96 sequences: 192, no column split (before, 32-row chunks half of padding)
+    p = sw.swattn_plan(desc(), 1, 188)
+    assert p.rows_per_chunk == 16 and p.row_chunks == 1 and p.grid == 48 * 4
+    p = sw.swattn_plan(desc(batch=96), 1, 188)
+    assert p.rows_per_chunk == 16 and p.grid == 192
     # 96 units (48 problems): four times over is 384 > 256, twice over 192 -> 16-row chunks
     # without the column split; 160 units: 32-row chunks
     p = sw.swattn_plan(desc(batch=48), 8, 188)

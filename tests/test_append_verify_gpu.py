@@ -21,7 +21,7 @@ pytestmark = pytest.mark.gpu
 FMT = {"bf16": sw.SWATTN_BF16, "f32": sw.SWATTN_F32}
 
 CASES = [
-    # one layer of the verify step: 16-row chunks, each over two workgroups (column halves)
+    # one layer of the verify step: 16-row chunks, each over four workgroups (column quarters)
     dict(id="one_layer", B=1, n_q=8, ctx=[4096]),
     # the verify workload's 24 layers
     dict(id="layers", B=24, n_q=8, ctx=[4096] * 24),

@@ -68,7 +68,7 @@ def test_split_invariance_and_determinism_mfma():
 def _workload_and_reference(key):
     if key == "one_layer":
         # one layer of the verify step (2 units): every split count keeps 16-row chunks,
-        # each run by two workgroups (column halves), so a chunk waits for S x 2 arrivals
+        # each run by four workgroups (column quarters), so a chunk waits for S x 4 arrivals
         w = synth.make_workload("one_layer", B=1, H=8, Hkv=2, D=256, n_q=8, window=188, ctx=4096, bs=16, seed=7,
                                 recent=195)
         return w, gu.reference(w)
@@ -102,7 +102,7 @@ def test_fused_merge_equals_merge_kernel(key, variant):
         kern = [call(q, S, sw.SWATTN_MERGE_KERNEL, None) for q in q_sets]
         assert kern[0][1].merge_grid > 0 and kern[0][1].fused_merge == 0
         if key == "one_layer":
-            assert kern[0][1].rows_per_chunk == 16 and kern[0][1].grid == 2 * 2 * 2 * S
+            assert kern[0][1].rows_per_chunk == 16 and kern[0][1].grid == 2 * 2 * 4 * S
         gu.check(kern[0][0], ref, w.kv_dtype, True, label=f"{key} S={S} merge kernel")
         plan = kern[0][1]
         ws = torch.zeros(plan.workspace_bytes, dtype=torch.uint8, device=gu.DEV)
@@ -528,3 +528,26 @@ def test_largest_queries_full_window(n_q, prefill):
     gu.log(f"  plan {plan.as_dict()}")
     assert plan.num_splits >= 8                      # 4096 + n_q - 1 keys, at most 512 per workgroup
     gu.check(got, ref, w.kv_dtype, True, label=f"largest n_q={n_q}")
+
+
+def test_column_splits_do_not_change_the_bits():
+    # the same sequences in launches that split a 16-row chunk's columns four ways (1
+    # problem), two ways (24 problems) and not at all (48 problems): identical output bits
+    w = synth.make_workload("colsplit", B=48, H=8, Hkv=2, D=256, n_q=8, window=188, ctx=None, bs=16, seed=120,
+                            ctx_range=(8, 3000), max_blocks=256)
+    t = gu.upload(w)
+    outs, splits = {}, {}
+    for nb in (48, 24, 1):
+        desc = sw.make_desc(t["q"][:nb], t["k"], t["bt"][:nb], int(w.ctx_len.max()), out_dtype=sw.SWATTN_F32)
+        plan = sw.swattn_plan(desc, w.n_q, w.window)
+        assert plan.rows_per_chunk == 16 and plan.num_splits == 1, plan.as_dict()
+        splits[nb] = plan.grid // (nb * w.Hkv * plan.row_chunks)
+        out = torch.empty(t["q"][:nb].shape, dtype=torch.float32, device=gu.DEV)
+        sw.swattn_verify(desc, t["q"][:nb], t["k"], t["v"], t["bt"][:nb], t["ctx"][:nb], w.n_q, w.window, w.scale,
+                         out, None, 0, torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        outs[nb] = out
+    assert splits == {48: 1, 24: 2, 1: 4}, splits
+    assert torch.equal(outs[48][:24].view(torch.int32), outs[24].view(torch.int32))
+    assert torch.equal(outs[48][:1].view(torch.int32), outs[1].view(torch.int32))
+    gu.check(outs[48].cpu().numpy().astype(np.float64), gu.reference(w), w.kv_dtype, True, label="colsplit")
