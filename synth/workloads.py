@@ -14,8 +14,10 @@ inputs stand in for the KV state of one stream with up to 4096 positions):
   older positions inside the sequence hold finite sentinels (K = +4, V = 100) and
   positions at or beyond ``ctx_len`` inside a referenced block hold NaN, so that a
   kernel that leaks weight outside the window, or reads past the context, shows;
-* the physical block pool is exactly the blocks the sequences reference, in a
-  random permutation; unused block-table entries are -1.
+* the physical block pool is the blocks the sequences reference, in a random
+  permutation, plus ``extra_blocks`` blocks that no table references, filled
+  with NaN (so that a read outside the referenced blocks shows); unused
+  block-table entries are -1.
 """
 from dataclasses import dataclass, field
 import math
@@ -86,7 +88,7 @@ class Workload:
 def make_workload(name, *, B, H, Hkv, D, n_q, window, ctx, bs, seed,
                   q_dtype=BF16, kv_dtype=BF16, scale=None, recent=None,
                   shuffle=True, hot_frac=0.0, hot_scale=8.0, max_blocks=None,
-                  ctx_range=None):
+                  ctx_range=None, extra_blocks=0):
     """Build one seeded workload.
 
     ctx: an int (same context for every sequence) or a sequence of ints; ignored
@@ -94,6 +96,9 @@ def make_workload(name, *, B, H, Hkv, D, n_q, window, ctx, bs, seed,
     drawn uniformly from the integers lo..hi inclusive.
     recent: how many of the most recent positions of each sequence hold random
     values (default: all of them).
+    extra_blocks: physical blocks added to the pool that no sequence references;
+    they hold NaN.  The table's blocks are the first ones of a permutation of the
+    whole pool (with 0 extra blocks the draws are those of the plain pool).
     """
     rng = np.random.default_rng(seed)
     if ctx_range is not None:
@@ -105,7 +110,8 @@ def make_workload(name, *, B, H, Hkv, D, n_q, window, ctx, bs, seed,
     nblk = [(int(c) + bs - 1) // bs for c in ctx_len]
     if max_blocks is None:
         max_blocks = max(nblk)
-    pool = int(sum(nblk))
+    used = int(sum(nblk))
+    pool = used + int(extra_blocks)
     perm = rng.permutation(pool) if shuffle else np.arange(pool)
     table = np.full((B, max_blocks), -1, dtype=np.int32)
     start = 0
@@ -184,49 +190,49 @@ def make_workload(name, *, B, H, Hkv, D, n_q, window, ctx, bs, seed,
                     q=q_store, k_cache=k_store, v_cache=v_store,
                     block_table=table, ctx_len=ctx_len.astype(np.int32),
                     k_scale=k_scale, v_scale=v_scale,
-                    meta=dict(seed=seed, recent=recent, shuffle=shuffle))
+                    meta=dict(seed=seed, recent=recent, shuffle=shuffle, extra_blocks=int(extra_blocks)))
 
 
-def _c0():
+def _c0(**kw):
     return make_workload("tiny_decode_fp32_d64_ctx300", B=1, H=2, Hkv=1, D=64, n_q=1,
                          window=188, ctx=300, bs=300, seed=0, q_dtype=F32,
-                         kv_dtype=F32, scale=1.0 / 8.0, recent=188, shuffle=False)
+                         kv_dtype=F32, scale=1.0 / 8.0, recent=188, shuffle=False, **kw)
 
 
-def _c1():
+def _c1(**kw):
     return make_workload("verify_24layers_h8kv2_d256_bf16_ctx4096_w188_nq8", B=24, H=8,
                          Hkv=2, D=256, n_q=8, window=188, ctx=4096, bs=16, seed=1,
-                         recent=188 + 8 - 1)
+                         recent=188 + 8 - 1, **kw)
 
 
-def _decode():
+def _decode(**kw):
     return make_workload("decode_24layers_h8kv2_d256_bf16_ctx4096_w188_nq1", B=24, H=8,
                          Hkv=2, D=256, n_q=1, window=188, ctx=4096, bs=16, seed=6,
-                         recent=188)
+                         recent=188, **kw)
 
 
-def _c2(ctx):
+def _c2(ctx, **kw):
     return make_workload(f"fullctx_24layers_h8kv2_d256_bf16_ctx{ctx}_w4096_nq8", B=24,
-                         H=8, Hkv=2, D=256, n_q=8, window=4096, ctx=ctx, bs=16, seed=2)
+                         H=8, Hkv=2, D=256, n_q=8, window=4096, ctx=ctx, bs=16, seed=2, **kw)
 
 
-def _c3():
+def _c3(**kw):
     return make_workload("wideverify_24layers_h8kv2_d256_bf16_ctx4096_w188_nq64", B=24,
                          H=8, Hkv=2, D=256, n_q=64, window=188, ctx=4096, bs=16, seed=3,
-                         recent=188 + 64 - 1, hot_frac=614 / 12288)
+                         recent=188 + 64 - 1, hot_frac=614 / 12288, **kw)
 
 
-def _c4(kv_dtype):
+def _c4(kv_dtype, **kw):
     return make_workload(f"batched_256seq_h8kv2_d256_{kv_dtype}kv_ctxU188-4096_w188_nq8",
                          B=256, H=8, Hkv=2, D=256, n_q=8, window=188, ctx=None, bs=16,
                          seed=4, kv_dtype=kv_dtype, recent=188 + 8 - 1,
-                         ctx_range=(188, 4096), max_blocks=256)
+                         ctx_range=(188, 4096), max_blocks=256, **kw)
 
 
-def _prefill(n_q):
+def _prefill(n_q, **kw):
     return make_workload(f"prefill_24layers_h8kv2_d256_bf16_ctx4096_w188_nq{n_q}", B=24, H=8, Hkv=2,
                          D=256, n_q=n_q, window=188, ctx=4096, bs=16, seed=5,
-                         recent=188 + n_q - 1)
+                         recent=188 + n_q - 1, **kw)
 
 
 # The five workloads of the build: tiny decode, single-stream verify, the
@@ -236,17 +242,18 @@ def _prefill(n_q):
 NAMED = {
     "tiny_decode": _c0,
     "verify": _c1,
-    "fullctx_1024": lambda: _c2(1024),
-    "fullctx_2048": lambda: _c2(2048),
-    "fullctx_4096": lambda: _c2(4096),
+    "fullctx_1024": lambda **kw: _c2(1024, **kw),
+    "fullctx_2048": lambda **kw: _c2(2048, **kw),
+    "fullctx_4096": lambda **kw: _c2(4096, **kw),
     "wide_verify": _c3,
-    "batched_fp8": lambda: _c4(E4M3),
-    "batched_bf16": lambda: _c4(BF16),
-    "prefill_512": lambda: _prefill(512),
+    "batched_fp8": lambda **kw: _c4(E4M3, **kw),
+    "batched_bf16": lambda **kw: _c4(BF16, **kw),
+    "prefill_512": lambda **kw: _prefill(512, **kw),
     "decode": _decode,
 }
 
 
-def named_workload(key):
-    return NAMED[key]()
+def named_workload(key, **overrides):
+    """A named workload; keyword overrides go to make_workload (e.g. extra_blocks)."""
+    return NAMED[key](**overrides)
 

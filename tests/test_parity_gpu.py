@@ -37,8 +37,8 @@ def test_named_workload(key):
     gu.check(got, ref, w.kv_dtype, out_f32=(w.q_dtype == "f32"), label=key)
 
 
-@pytest.mark.parametrize("key", ["verify", "wide_verify", "batched_fp8", "batched_bf16", "fullctx_2048",
-                                 "prefill_512"])
+@pytest.mark.parametrize("key", ["verify", "decode", "wide_verify", "batched_fp8", "batched_bf16", "fullctx_1024",
+                                 "fullctx_2048", "fullctx_4096", "prefill_512"])
 def test_named_workload_f32_out(key):
     gu.log(f"[named f32 out] {key}")
     w, ref = gu.named(key)
@@ -551,3 +551,55 @@ def test_column_splits_do_not_change_the_bits():
     assert torch.equal(outs[48][:24].view(torch.int32), outs[24].view(torch.int32))
     assert torch.equal(outs[48][:1].view(torch.int32), outs[1].view(torch.int32))
     gu.check(outs[48].cpu().numpy().astype(np.float64), gu.reference(w), w.kv_dtype, True, label="colsplit")
+
+
+# ---------------------------------------------------------------------------
+# NaN in pool blocks that no table references: a read outside the referenced
+# blocks would turn outputs into NaN
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("key", ["verify", "decode", "batched_fp8", "batched_bf16"])
+def test_nan_in_unreferenced_blocks(key):
+    gu.log(f"[nan blocks] {key}")
+    w = synth.named_workload(key, extra_blocks=384)
+    ref = gu.reference(w)
+    got, plan = gu.run(w)
+    gu.log(f"  plan {plan.as_dict()}")
+    gu.check(got, ref, w.kv_dtype, False, label=f"{key} + NaN blocks")
+    got32, _ = gu.run(w, out_f32=True)
+    gu.check(got32, ref, w.kv_dtype, True, label=f"{key} + NaN blocks f32")
+
+
+@pytest.mark.parametrize("case", fuzz_cases()[:16], ids=lambda c: f"nanfz{c['idx']}")
+def test_fuzz_nan_in_unreferenced_blocks(case):
+    c = case
+    w = synth.make_workload(f"nanfz{c['idx']}", B=c["B"], H=c["G"] * c["Hkv"], Hkv=c["Hkv"], D=c["D"],
+                            n_q=c["n_q"], window=c["window"], ctx=c["ctx"], bs=c["bs"],
+                            seed=300 + c["idx"], q_dtype=c["qd"], kv_dtype=c["kd"], extra_blocks=7,
+                            recent=(c["window"] + c["n_q"] - 1) if c["sentinels"] else None)
+    ref = gu.reference(w)
+    got, plan = gu.run(w, out_f32=True, num_splits=c["S"])
+    gu.log(f"[nan fuzz] {c} plan {plan.as_dict()}")
+    gu.check(got, ref, w.kv_dtype, True, label=f"nanfz{c['idx']}")
+
+
+# ---------------------------------------------------------------------------
+# normalisation: V = 1 on every window position gives out = 1 (sentinels V = 100
+# stay on the older positions, NaN past the context)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("variant,kv", [(sw.SWATTN_VARIANT_MFMA, "bf16"), (sw.SWATTN_VARIANT_MFMA, "e4m3"),
+                                        (sw.SWATTN_VARIANT_VALU, "bf16"), (sw.SWATTN_VARIANT_VALU, "e4m3")])
+def test_all_ones_values_give_one(variant, kv):
+    w = synth.make_workload("ones", B=4, H=8, Hkv=2, D=256, n_q=8, window=188, ctx=[4096, 300, 195, 9], bs=16,
+                            seed=31, recent=195, max_blocks=256, kv_dtype=kv)
+    lo, hi = oracle.window_bounds(w.ctx_len, w.n_q, w.window)
+    one = synth.to_bf16_bits(np.float32([1.0]))[0] if kv == "bf16" else np.uint8(0x38)   # E4M3 0.0111.000 = 1
+    for b in range(w.B):
+        for j in range(int(lo[b, 0]), int(hi[b, -1]) + 1):
+            w.v_cache[w.block_table[b, j // w.bs], :, j % w.bs, :] = one
+    if kv == "e4m3":
+        w.v_scale[:] = 1.0
+    for out_f32 in (True, False):
+        got, plan = gu.run(w, out_f32=out_f32, variant=variant)
+        gu.log(f"[ones] variant {variant} kv {kv} f32 {out_f32}: max |out-1| {np.abs(got - 1).max():.3e}")
+        # within bfloat16 rounding: one bf16 step below 1 is 2^-8
+        assert np.isfinite(got).all() and np.abs(got - 1.0).max() <= 2.0 ** -8
