@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define SWATTN_ABI_VERSION 2
+#define SWATTN_ABI_VERSION 3
 #define SWATTN_MAX_NQ 64          /* SPLITKV_VERIFY_MAX_Q of the manifest */
 #define SWATTN_MAX_PREFILL_NQ 512 /* MAX_NUM_BATCHED_TOKENS of the manifest */
 
@@ -79,9 +79,10 @@ typedef enum {
                                      e.g. decode) and the launch has few enough row chunks,
                                      else the merge kernel */
     SWATTN_MERGE_KERNEL = 1,      /* a separate merge kernel after the partition kernel */
-    SWATTN_MERGE_FUSED = 2        /* the last partition workgroup of each row chunk combines;
-                                     SWATTN_ERR_SHAPE when the launch has more row chunks
-                                     (B * Hkv * row_chunks) than counters */
+    SWATTN_MERGE_FUSED = 2        /* the last partition workgroup of each merge group (row chunk x
+                                     column split) combines; SWATTN_ERR_SHAPE when the launch has
+                                     more groups (B * Hkv * row_chunks * col_splits) than
+                                     counters (SWATTN_WORKSPACE_COUNTER_BYTES / 4) */
 } swattn_merge_t;
 
 /* Problem description.  Plain data; the caller owns it. */
@@ -102,6 +103,12 @@ typedef struct {
     int32_t num_splits;           /* 0: library chooses; > 0 forces the KV split count */
     int32_t variant;              /* swattn_variant_t; AUTO lets the library choose */
     int32_t merge;                /* swattn_merge_t: how split partials are combined */
+    /* Tuning overrides of the matrix-core launch (0: library chooses).  They force a
+     * geometry; SWATTN_ERR_ARG when the plan is not the matrix-core variant or the value
+     * is not offered for this shape. */
+    int32_t rows_per_chunk;       /* 16 (head_dim 256 only) or 32 query rows per workgroup */
+    int32_t col_splits;           /* 1, 2 or 4 workgroups per row chunk, each with D/col_splits
+                                     output columns (head_dim 256 only) */
 } swattn_desc_t;
 
 /* What swattn_verify will launch for a description (filled by swattn_plan). */
@@ -112,9 +119,14 @@ typedef struct {
     int32_t row_chunks;           /* row chunks per (problem, KV head) */
     int32_t grid;                 /* workgroups of the partition kernel */
     int32_t merge_grid;           /* workgroups of the merge kernel (0 when S == 1 or fused) */
-    int32_t fused_merge;          /* 1: the last partition workgroup of each row chunk to
-                                     finish combines the S partials itself (no merge kernel) */
+    int32_t fused_merge;          /* 1: the last partition workgroup of each merge group (row
+                                     chunk x column split) to finish combines the group's S
+                                     partials itself (no merge kernel) */
     size_t workspace_bytes;       /* device scratch swattn_verify needs (0 when S == 1) */
+    int32_t col_splits;           /* workgroups per row chunk, each with D/col_splits output
+                                     columns (matrix-core variant; 1 otherwise) */
+    int32_t tile_keys;            /* keys per LDS tile of the matrix-core kernel (32 or 64;
+                                     0 for the vector-ALU variant) */
 } swattn_plan_t;
 
 /* A split plan's workspace starts with this many bytes of arrival counters, the

@@ -53,6 +53,7 @@ class swattn_desc_t(ctypes.Structure):
         ("q_dtype", ctypes.c_int), ("kv_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int),
         ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
         ("num_splits", ctypes.c_int32), ("variant", ctypes.c_int32), ("merge", ctypes.c_int32),
+        ("rows_per_chunk", ctypes.c_int32), ("col_splits", ctypes.c_int32),
     ]
 
 
@@ -61,7 +62,7 @@ class swattn_plan_t(ctypes.Structure):
         ("variant", ctypes.c_int32), ("num_splits", ctypes.c_int32),
         ("rows_per_chunk", ctypes.c_int32), ("row_chunks", ctypes.c_int32),
         ("grid", ctypes.c_int32), ("merge_grid", ctypes.c_int32), ("fused_merge", ctypes.c_int32),
-        ("workspace_bytes", ctypes.c_size_t),
+        ("workspace_bytes", ctypes.c_size_t), ("col_splits", ctypes.c_int32), ("tile_keys", ctypes.c_int32),
     ]
 
     def as_dict(self):
@@ -69,7 +70,7 @@ class swattn_plan_t(ctypes.Structure):
 
 
 _lib = None
-ABI_VERSION = 2          # SWATTN_ABI_VERSION these ctypes mirrors follow
+ABI_VERSION = 3          # SWATTN_ABI_VERSION these ctypes mirrors follow
 
 
 def lib():
@@ -272,7 +273,7 @@ def _dtype_code(t):
 
 
 def make_desc(q, k_cache, block_table, max_ctx_len, out_dtype=None, k_scale=None, v_scale=None,
-              num_splits=0, variant=SWATTN_VARIANT_AUTO, merge=SWATTN_MERGE_AUTO):
+              num_splits=0, variant=SWATTN_VARIANT_AUTO, merge=SWATTN_MERGE_AUTO, rows_per_chunk=0, col_splits=0):
     """Descriptor for q [B, n_q, H, D], k_cache [num_blocks, Hkv, bs, D],
     block_table [B, max_blocks]; out_dtype defaults to q's dtype."""
     B, _, H, D = q.shape
@@ -289,20 +290,22 @@ def make_desc(q, k_cache, block_table, max_ctx_len, out_dtype=None, k_scale=None
     d.num_splits = int(num_splits)
     d.variant = int(variant)
     d.merge = int(merge)
+    d.rows_per_chunk = int(rows_per_chunk)
+    d.col_splits = int(col_splits)
     return d
 
 
 def verify(q, k_cache, v_cache, block_table, ctx_len, n_q, window, scale, max_ctx_len,
            out=None, out_dtype=None, k_scale=None, v_scale=None, num_splits=0,
            variant=SWATTN_VARIANT_AUTO, workspace=None, stream=None, prefill=False,
-           merge=SWATTN_MERGE_AUTO):
+           merge=SWATTN_MERGE_AUTO, rows_per_chunk=0, col_splits=0):
     """Run swattn_verify (or swattn_prefill) on torch device tensors; returns (out, plan).
 
     Allocates ``out`` and a zero-filled workspace with torch when they are not given
     (a caller under graph capture passes both)."""
     import torch
     desc = make_desc(q, k_cache, block_table, max_ctx_len, out_dtype, k_scale, v_scale,
-                     num_splits, variant, merge)
+                     num_splits, variant, merge, rows_per_chunk, col_splits)
     plan = (swattn_prefill_plan if prefill else swattn_plan)(desc, n_q, window)
     if out is None:
         tdt = torch.float32 if desc.out_dtype == SWATTN_F32 else torch.bfloat16

@@ -107,22 +107,12 @@ swattn_status_t prepare_attend(const swattn_desc_t* d, const void* q, const void
     p.S = plan.num_splits;
     p.rows_per_chunk = plan.rows_per_chunk;
     p.row_chunks = plan.row_chunks;
-    p.col_splits = (int32_t)((int64_t)plan.grid / ((int64_t)d->batch * d->num_kv_heads * plan.row_chunks * plan.num_splits));
+    p.col_splits = plan.col_splits;
     p.q_dtype = d->q_dtype;
     p.kv_dtype = d->kv_dtype;
     p.out_dtype = d->out_dtype;
     p.scale_log2 = (float)((double)scale * 1.4426950408889634);   // log2(e)
-    // Matrix-core tiles: 64 keys, unless a workgroup with 64-key tiles needs a CU's
-    // whole LDS (bfloat16, head_dim 256) and there are more units than CUs: then
-    // 32-key tiles let two workgroups share a CU, so twice the units run at once.
-    {
-        const int64_t kv_elt = d->kv_dtype == SWATTN_FP8_E4M3 ? 1 : (d->kv_dtype == SWATTN_BF16 ? 2 : 4);
-        const int64_t tile64 = 64 * (int64_t)d->head_dim * kv_elt;
-        const bool one_per_cu = 2 * (4 * tile64 + 14 * 1024) > 160 * 1024;
-        const int64_t units = (int64_t)d->batch * d->num_kv_heads * plan.row_chunks * plan.num_splits;
-        p.tile_keys = (plan.variant == SWATTN_VARIANT_MFMA && one_per_cu && units > kComputeUnits &&
-                       plan.rows_per_chunk == kMfmaRows) ? 32 : 64;
-    }
+    p.tile_keys = plan.tile_keys;
 
     MergeParams& m = call->m;
     {

@@ -70,10 +70,10 @@ struct Geo {
     static constexpr int kNiK = kT / kRpi;                  // load instructions per K (or V) tile
     static constexpr int kTileB = kT * kRowB;               // bytes of one K tile
     static_assert(kCpr >= 4 && kCpr <= 64 && kNiK * 1024 == kTileB, "tile geometry");
-    // 16-row chunks may also split the output columns between two or four workgroups:
-    // each loads whole K rows (all compute the chunk's scores) and its own part of every
-    // V row.
-    static_assert(CS == 1 || ((CS == 2 || CS == 4) && RB == 1), "column splits of 16-row chunks only");
+    // Row chunks may also split the output columns between two or four workgroups: each
+    // loads whole K rows (all compute the chunk's scores) and its own part of every V
+    // row.
+    static_assert(CS == 1 || ((CS == 2 || CS == 4) && KT == 64), "column splits with 64-key tiles only");
     static constexpr int kCS = CS;                          // column splits
     static constexpr int kRowBV = kRowB / kCS;              // bytes of a V row this workgroup loads
     static constexpr int kCprV = kRowBV / 16;
@@ -82,16 +82,30 @@ struct Geo {
     static constexpr int kTileBV = kT * kRowBV;
     static_assert(kCprV >= 4 && kNiV * 1024 == kTileBV, "V tile geometry");
     static constexpr int kStageB = kTileB + kTileBV;
-    // Stages of the K/V ring: four where two workgroups per CU still fit with them (up
-    // to three tiles in flight absorb the tail latency of a loaded memory system),
-    // else two.
+    // Q rows of the chunk, staged once per workgroup in LDS (bfloat16, kRows x D):
+    // every compute wave reads its Q^T operand from there.
+    static constexpr int kRowQ = D * 2;
+    static constexpr int kCprQ = kRowQ / 16;
+    static constexpr int kQB = 16 * RB * kRowQ;
+    static constexpr int kNiQ = kQB / 1024;                 // load instructions of the Q rows
+    static_assert(kNiQ * 1024 == kQB, "Q geometry");
+    // Stages of the K/V ring (the ring plus < 14 KiB of tables per workgroup, 160 KiB
+    // of LDS per CU): four where two workgroups per CU still fit with them (up to three
+    // tiles in flight absorb the tail latency of a loaded memory system), else two.
+    // (A CU's load rate, about 30-45 GB/s, bounds these chains: rings that request
+    // every tile of a chunk up front measured slower, since tile 0 then lands later.)
     static constexpr int kNS = 2 * (4 * kStageB + 14 * 1024) <= 160 * 1024 ? 4 : 2;
-    // Workgroups per CU that the LDS allows (the ring plus < 14 KiB of tables each,
-    // 160 KiB per CU).  Where only one fits, the workgroup splits the output columns
-    // across two wave sets (8 waves) so that every SIMD still holds two waves;
-    // otherwise it has 4 waves.  Either way a SIMD runs two waves, so each may hold
-    // 256 registers.
+    // Workgroups per CU that the LDS allows.  Where only one fits, the workgroup splits
+    // the output columns across two wave sets (8 waves) so that every SIMD still holds
+    // two waves; otherwise it has 4 waves.  Either way a SIMD runs two waves, so each
+    // may hold 256 registers.
     static constexpr int kBlocks = 2 * (kNS * kStageB + 14 * 1024) <= 160 * 1024 ? 2 : 1;
+    // Where two workgroups share a CU, the prologue leaves the last ring stage free
+    // (its tile goes out with tile 0's scores): Q is staged there.  Otherwise it has a
+    // region of its own.
+    static constexpr bool kQAlias = kBlocks == 2;
+    static_assert(!kQAlias || kTileB >= kQB, "Q fits the K part of a ring stage");
+    static_assert(kQAlias || kNS * kStageB + 14 * 1024 + kQB <= 160 * 1024, "one workgroup's LDS");
     // column sets: 64-key tiles split them only where one workgroup fills the CU;
     // 32-key tiles always split them in two (their waves do not split the keys)
     static constexpr int kND = kSplitKeys ? (kBlocks == 2 ? 1 : 2) : 2;
@@ -110,11 +124,13 @@ struct Geo {
     static constexpr int kNT = kNW * 64;
     static constexpr int kShare = (kNiK + kNiV) / kNW;      // load instructions per wave per tile
     static_assert(kShare * kNW == kNiK + kNiV && kShare <= 16, "loads split evenly over the waves");
-    static_assert(kNS == 2 || kNS == 4, "ring of 2 or 4 stages");
+    static_assert(kNS >= 2 && kNS <= 4, "ring of 2 to 4 stages");
     static_assert(kNS * kShare < 64, "a wave's loads in flight must fit the vmcnt counter");
     // K rows: chunk c of row k is stored at c ^ swz_k(k); 16 consecutive rows (the
     // 16 lanes of an A-operand read) land on distinct bank groups.
     static __device__ __forceinline__ int swz_k(int k) { return k & (kCpr >= 16 ? 15 : kCpr - 1); }
+    // Q rows: the same scheme for the B-operand reads of 16 consecutive rows
+    static __device__ __forceinline__ int swz_q(int r) { return r & (kCprQ >= 16 ? 15 : kCprQ - 1); }
     // V rows (this workgroup's part of them): a transpose read takes keys {4q + r} and
     // {16 + 4q + r} of a 32-key half together (r < 4), so the swizzle separates r and
     // bit 4 of the key.
@@ -219,6 +235,9 @@ __global__ __launch_bounds__((Geo<D, FP8, KT, RB, CS>::kNT), (Geo<D, FP8, KT, RB
     __shared__ __attribute__((aligned(16))) const unsigned char* vptr[kMfmaMaxKeys];
     __shared__ int tbl[NT];
     __shared__ float xstat[2][2][2][16];         // [rb][kh][m, l][row]
+    // the chunk's Q rows: the K part of the last ring stage where two workgroups share a
+    // CU, else a region of their own (in the K stages' array, past the ring)
+    __shared__ __attribute__((aligned(16))) unsigned char qst[G::kQAlias ? 16 : G::kQB];
     static_assert(2 * 2 * 16 * (D / 2) * 4 <= (int)sizeof(kst), "merge exchange fits in the K stages");
 
     const int tid = threadIdx.x;
@@ -240,24 +259,45 @@ __global__ __launch_bounds__((Geo<D, FP8, KT, RB, CS>::kNT), (Geo<D, FP8, KT, RB
     const int g = blockIdx.x % p.Hkv;
     const int b = blockIdx.x / p.Hkv;
 
+    // The chunk's Q rows go into LDS at once, once per workgroup, each wave issuing a
+    // share (waves of every role: with the loader waves alone issuing them, the E4M3
+    // 16-row kernel needs more registers than two waves per SIMD allow); a row past R
+    // loads a valid row.  They land while ctx_len and the block table are fetched and
+    // are waited for before the block-table barrier, so the compute waves read their
+    // Q^T operands from LDS without a barrier of their own, and no tile competes with
+    // them for the CU's load rate.
+#pragma unroll
+    for (int jj = 0; jj < (G::kNiQ + G::kNW - 1) / G::kNW; ++jj) {
+        const int j = wave + jj * G::kNW;                            // wave-uniform
+        if (j < G::kNiQ) {
+            const int slot = j * 64 + lane;
+            const int row = slot / G::kCprQ, pc = slot % G::kCprQ;
+            const int r = min(rc * G::kRows + row, p.R - 1);
+            const int i = r / p.G, h = g * p.G + (r - i * p.G);
+            const unsigned char* src = reinterpret_cast<const unsigned char*>(p.q) +
+                                       (((int64_t)b * p.n_q + i) * p.H + h) * G::kRowQ + ((pc ^ G::swz_q(row)) << 4);
+            if constexpr (G::kQAlias)
+                dma16(src, &kst[NS - 1][j * 1024]);
+            else
+                dma16(src, &qst[j * 1024]);
+        }
+    }
+
     // A block-table row that fits one entry per thread is read while ctx_len is in
     // flight, which removes one dependent round trip to memory.
     const bool short_row = p.max_blocks <= NT;
     const int tb = (short_row && tid < p.max_blocks) ? p.block_table[(int64_t)b * p.max_blocks + tid] : 0;
 
-    // Q^T operand of this lane: row rb*16 + l16, dims ks*32 + q4*8 .. +7, loaded
-    // straight into registers.  A row past R loads a valid row instead; its window
-    // is empty and it is never written.
+    // this lane's query row (row rb*16 + l16 of the chunk); a row past R has an empty
+    // window and is never written
     const int qrow = rc * G::kRows + rb * 16 + l16;
     const bool qvalid = qrow < p.R;
     const int qi = qvalid ? qrow / p.G : 0;
-    uint4 qreg[KS];
-    {
-        const int h = g * p.G + (qvalid ? qrow - qi * p.G : 0);
-        const uint16_t* qp =
-            reinterpret_cast<const uint16_t*>(p.q) + (((int64_t)b * p.n_q + qi) * p.H + h) * D + q4 * 8;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qreg[ks] = loader ? make_uint4(0u, 0u, 0u, 0u) : ld_global_16(qp + ks * 32);
+    float scale_log2 = p.scale_log2;
+    float out_scale = 1.0f;
+    if constexpr (FP8) {
+        scale_log2 *= p.k_scale[g];
+        out_scale = p.v_scale[g];
     }
 
     const int ctx = p.ctx_len[b];
@@ -277,7 +317,8 @@ __global__ __launch_bounds__((Geo<D, FP8, KT, RB, CS>::kNT), (Geo<D, FP8, KT, RB
     }
     const int ntiles = (nk + kT - 1) / kT;
     if (short_row) tbl[tid] = tb;
-    __syncthreads();   // tbl is in LDS
+    wait_vmcnt<0>();   // this wave's share of the Q rows has landed too
+    __syncthreads();   // tbl and the Q rows are in LDS
 
     // ---- key -> source rows: cache row (phys * Hkv + g) * bs + off of K and V; keys
     //      past the split read the zero row, keys in a bad block a NaN K and zero V row
@@ -352,16 +393,9 @@ __global__ __launch_bounds__((Geo<D, FP8, KT, RB, CS>::kNT), (Geo<D, FP8, KT, RB
 
     const int row_lo = qvalid ? max(0, pos0 + qi - p.window + 1) : 1;
     const int row_hi = qvalid ? pos0 + qi : 0;
-    float scale_log2 = p.scale_log2;
-    float out_scale = 1.0f;
-    if constexpr (FP8) {
-        scale_log2 *= p.k_scale[g];
-        out_scale = p.v_scale[g];
-    }
 
-    // The compiler cannot see the loads below, so its own wait before the first use
-    // of qreg would count them as older: the Q rows (issued with ctx_len, so landed
-    // by now) are waited for here instead, before any of them is issued.
+    // The compiler cannot see the loads below, so a wait of its own for an earlier
+    // load would count them as older: nothing it issued is left in flight from here.
     wait_vmcnt<0>();
     // The first tiles go out together, one per stage: all NS where one workgroup has
     // the CU, NS-1 where two share it (tile NS-1 then goes out with tile 0's scores:
@@ -372,6 +406,23 @@ __global__ __launch_bounds__((Geo<D, FP8, KT, RB, CS>::kNT), (Geo<D, FP8, KT, RB
     for (int t = 0; t < kPro; ++t)
         if (t < ntiles) issue_range(t, 0, SH);
 
+    // Q^T operand of this lane: row rb*16 + l16, dims ks*32 + q4*8 .. +7, from the Q
+    // rows in LDS (landed before the block-table barrier).  The barrier of tile 0 orders
+    // these reads before tile NS-1 goes into the stage that Q may share.
+    uint4 qreg[KS];
+    if (ntiles > 0) {
+        if (!loader) {
+            const int row = rb * 16 + l16;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int off = row * G::kRowQ + (((ks * 4 + q4) ^ G::swz_q(row)) << 4);
+                if constexpr (G::kQAlias)
+                    qreg[ks] = *reinterpret_cast<const uint4*>(&kst[NS - 1][off]);
+                else
+                    qreg[ks] = *reinterpret_cast<const uint4*>(&qst[off]);
+            }
+        }
+    }
     float m_run = -INFINITY, l_run = 0.0f;   // row l16 of block rb, keys of half kh
     f32x4_t o[DB];                           // lane holds O^T[dcol0 + db*16 + 4*q4 + e][row l16]
     const int dcol0 = dh * DH;
@@ -601,7 +652,9 @@ __global__ __launch_bounds__((Geo<D, FP8, KT, RB, CS>::kNT), (Geo<D, FP8, KT, RB
                 store_partial4(p, p.ws_o + prow * D + cs * DC + dcol0 + db * 16 + q4 * 4, v);
             }
         }
-        if (p.S > 1 && cs == 0 && dh == 0 && q4 == 0)
+        // every column split writes the row's log2-sum-exp (the same bits: all compute the
+        // same scores), so each merge group finds it among its own group's writes
+        if (p.S > 1 && dh == 0 && q4 == 0)
             store_partial1(p, p.ws_lse + prow, (l_run == 0.0f ? -INFINITY : m_run + log2f(l_run)) + poison);
         }
     } else {
@@ -609,14 +662,20 @@ __global__ __launch_bounds__((Geo<D, FP8, KT, RB, CS>::kNT), (Geo<D, FP8, KT, RB
     // ---- merge the two key halves of each row block, then write ---------------------
     // Wave (rb, kh, dh) keeps columns dcol0 + [kh*DH/2, kh*DH/2 + DH/2) and hands the
     // other half of its O^T, with its (max, sum), to its partner (rb, 1 - kh, dh).
+    // The exchanged rows are DH/2 floats long: their 16-byte chunks are XOR-swizzled by
+    // row so that the 16 rows of a wave's access fall on distinct LDS banks (unswizzled,
+    // a row stride of 512 bytes puts all 16 on the same banks: the exchange of the
+    // batched E4M3 workload took 3 us of an 18.5 us workgroup).
+    constexpr int kXch = DH / 8;                                // 16-byte chunks per exchanged row
+    const int xsw = l16 & (kXch >= 16 ? 15 : kXch - 1);
     __syncthreads();   // every wave is done with the stages
     float* xo = reinterpret_cast<float*>(&kst[0][0]);          // [rb][writer kh][dh][16 rows][DH/2]
     if (!loader) {
         float* dst = xo + (((rb * 2 + kh) * G::kND + dh) * 16 + l16) * (DH / 2);
 #pragma unroll
         for (int db = 0; db < DB / 2; ++db) {
-            const int dl = db * 16 + q4 * 4;                   // column within the half
-            *reinterpret_cast<f32x4_t*>(dst + dl) = pick(kh, o[db], o[DB / 2 + db]);
+            const int ch = (db * 4 + q4) ^ xsw;                // columns db*16 + 4*q4 .. +3 of the half
+            *reinterpret_cast<f32x4_t*>(dst + ch * 4) = pick(kh, o[db], o[DB / 2 + db]);
         }
         if (dh == 0 && q4 == 0) {
             xstat[rb][kh][0][l16] = m_run;
@@ -642,7 +701,7 @@ __global__ __launch_bounds__((Geo<D, FP8, KT, RB, CS>::kNT), (Geo<D, FP8, KT, RB
     const int64_t prow = (((int64_t)b * p.Hkv + g) * p.S + s) * p.R + qrow;
 #pragma unroll
     for (int db = 0; db < DB / 2; ++db) {
-        const f32x4_t other = *reinterpret_cast<const f32x4_t*>(src + db * 16 + q4 * 4);
+        const f32x4_t other = *reinterpret_cast<const f32x4_t*>(src + ((db * 4 + q4) ^ xsw) * 4);
         const f32x4_t mine = pick(kh, o[DB / 2 + db], o[db]);
         // key half 0's term first whichever wave finalises the column, so that the
         // result does not depend on how a launch splits the columns
@@ -665,7 +724,9 @@ __global__ __launch_bounds__((Geo<D, FP8, KT, RB, CS>::kNT), (Geo<D, FP8, KT, RB
             store_partial4(p, p.ws_o + prow * D + cs * DC + mcol + db * 16 + q4 * 4, v);
         }
     }
-    if (p.S > 1 && cs == 0 && kh == 0 && dh == 0 && q4 == 0)
+    // every column split writes the row's log2-sum-exp (the same bits: all compute the
+    // same scores), so each merge group finds it among its own group's writes
+    if (p.S > 1 && kh == 0 && dh == 0 && q4 == 0)
         store_partial1(p, p.ws_lse + prow, (l_all == 0.0f ? -INFINITY : m_all + log2f(l_all)) + poison);
     }
     }
@@ -693,8 +754,9 @@ __global__ __launch_bounds__((Geo<D, FP8, KT, RB, CS>::kNT), (Geo<D, FP8, KT, RB
         }
     }
 
-    // ---- split launches: the last workgroup of the row chunk combines the partials
-    if (p.counters != nullptr) merge_if_last<D, OUT_F32, NT>(p, b, g, rc, p.S * G::kCS);
+    // ---- split launches: the last workgroup of the (row chunk, column split) group
+    //      combines the group's partials
+    if (p.counters != nullptr) merge_if_last<D, OUT_F32, NT>(p, b, g, rc, cs);
 }
 
 
@@ -729,15 +791,21 @@ int launch_d(const PartitionParams& p, int grid, hipStream_t st) {
     // 32-key tiles exist for the one case where a 64-key workgroup fills a CU's LDS:
     // bfloat16 caches with head_dim 256
     if constexpr (D == 256) {
-        if (p.tile_keys == 32 && p.kv_dtype == SWATTN_BF16 && p.rows_per_chunk == 32)
+        if (p.tile_keys == 32 && p.kv_dtype == SWATTN_BF16 && p.rows_per_chunk == 32 && p.col_splits == 1)
             return launch_dk<D, 32, false, 2>(p, grid, st);
-        // 16-row chunks: bfloat16 and E4M3 caches with 64-key tiles
-        if (p.tile_keys == 64 && p.rows_per_chunk == 16)
+        if (p.tile_keys != 64) return (int)hipErrorInvalidValue;
+        // 16-row chunks, and 32-row chunks split by columns: bfloat16 and E4M3 caches
+        if (p.rows_per_chunk == 16)
             return p.col_splits == 4   ? launch_dk<D, 64, true, 1, 4>(p, grid, st)
                    : p.col_splits == 2 ? launch_dk<D, 64, true, 1, 2>(p, grid, st)
                                        : launch_dk<D, 64, true, 1, 1>(p, grid, st);
+        if (p.rows_per_chunk == 32)
+            return p.col_splits == 4   ? launch_dk<D, 64, true, 2, 4>(p, grid, st)
+                   : p.col_splits == 2 ? launch_dk<D, 64, true, 2, 2>(p, grid, st)
+                                       : launch_dk<D, 64, true, 2, 1>(p, grid, st);
+        return (int)hipErrorInvalidValue;
     }
-    if (p.tile_keys == 64 && p.rows_per_chunk == 32) return launch_dk<D, 64, true, 2>(p, grid, st);
+    if (p.tile_keys == 64 && p.rows_per_chunk == 32 && p.col_splits == 1) return launch_dk<D, 64, true, 2>(p, grid, st);
     return (int)hipErrorInvalidValue;
 }
 

@@ -323,12 +323,13 @@ __global__ __launch_bounds__(kBlockThreads) void partition_valu_kernel(Partition
                 store_partial1(p, p.ws_lse + prow, (L == 0.0f ? -INFINITY : rstat[rr][0] + log2f(L)) + poison);
         }
     }
-    // split launches: the last workgroup of the row chunk combines the partials
+    // split launches: the last workgroup of the row chunk combines the partials (one
+    // column split: the group is the whole chunk)
     if (p.counters != nullptr) {
         if (p.out_dtype == SWATTN_F32)
-            merge_if_last<D, true, kBlockThreads>(p, b, g, rc, p.S);
+            merge_if_last<D, true, kBlockThreads>(p, b, g, rc, 0);
         else
-            merge_if_last<D, false, kBlockThreads>(p, b, g, rc, p.S);
+            merge_if_last<D, false, kBlockThreads>(p, b, g, rc, 0);
     }
 }
 

@@ -89,6 +89,13 @@ swattn_status_t make_plan(const swattn_desc_t* d, int32_t n_q, int32_t window, i
 
     int64_t rows_per_chunk, S;
     int64_t col_splits = 1;
+    int64_t tile_keys = 0;
+    const bool forced_geo = d->rows_per_chunk != 0 || d->col_splits != 0;
+    if (forced_geo) {
+        if (variant != SWATTN_VARIANT_MFMA) return SWATTN_ERR_ARG;
+        if (!dtype_in(d->rows_per_chunk, {0, 16, 32}) || !dtype_in(d->col_splits, {0, 1, 2, 4})) return SWATTN_ERR_ARG;
+        if ((d->rows_per_chunk == 16 || d->col_splits > 1) && d->head_dim != 256) return SWATTN_ERR_ARG;
+    }
     if (variant == SWATTN_VARIANT_MFMA) {
         rows_per_chunk = kMfmaRows;
         const int64_t s_min = (U + kMfmaMaxKeys - 1) / kMfmaMaxKeys;
@@ -126,6 +133,14 @@ swattn_status_t make_plan(const swattn_desc_t* d, int32_t n_q, int32_t window, i
             rows_per_chunk = kMfmaRows / 2;
             col_splits = 4 * g16 <= kComputeUnits ? 4 : (2 * g16 <= kComputeUnits ? 2 : 1);
         }
+        if (d->rows_per_chunk != 0) rows_per_chunk = d->rows_per_chunk;
+        if (d->col_splits != 0) col_splits = d->col_splits;
+        // Tiles of 64 keys, or 32 where a 64-key workgroup needs a CU's whole LDS (bfloat16
+        // cache, head_dim 256, 32-row chunks, no column split) and there are more
+        // workgroups than CUs: 32-key tiles let two workgroups share a CU.
+        const bool one_per_cu = d->kv_dtype == SWATTN_BF16 && d->head_dim == 256;
+        const int64_t wgs = (int64_t)d->batch * d->num_kv_heads * ((R + rows_per_chunk - 1) / rows_per_chunk) * S;
+        tile_keys = (one_per_cu && rows_per_chunk == kMfmaRows && col_splits == 1 && wgs > kComputeUnits) ? 32 : 64;
     } else {
         rows_per_chunk = kValuRowsPerChunk;
         const int64_t row_chunks = (R + rows_per_chunk - 1) / rows_per_chunk;
@@ -149,19 +164,19 @@ swattn_status_t make_plan(const swattn_desc_t* d, int32_t n_q, int32_t window, i
     int32_t fused = 0;
     size_t ws = 0;
     if (S > 1) {
-        // The last workgroup of each row chunk combines the partials (no second launch)
-        // when the chunks fit the counter region and the chunk's partials are small
-        // (at most kFusedMaxPartialBytes: one workgroup reads them all, from past its
-        // L2); otherwise a merge kernel spreads the combination over many workgroups.
-        // Measured (MI355X, cold): tiny decode at S = 3 (1.5 KiB of partials), 13.5 ->
-        // 12.6 us; one layer of the verify step at S = 4 (128 KiB), +2 us per call;
-        // full context 4096 at S = 8 (256 KiB), 49 -> 54 us.
-        const int64_t chunks_total = (int64_t)d->batch * d->num_kv_heads * row_chunks;
-        if (d->merge == SWATTN_MERGE_FUSED && chunks_total > kMergeCounters) return SWATTN_ERR_SHAPE;
-        const int64_t chunk_partial_bytes = std::min<int64_t>(rows_per_chunk, R) * D * S * 4;
+        // The last workgroup of each merge group (row chunk x column split) combines the
+        // group's partials (no second launch) when the groups fit the counter region and
+        // a group's partials are small (at most kFusedMaxPartialBytes: one workgroup
+        // reads them all, from past its L2); otherwise a merge kernel spreads the
+        // combination over many workgroups.  Measured (MI355X, cold): tiny decode at
+        // S = 3 (1.5 KiB of partials), 13.5 -> 12.6 us; one layer of the verify step at
+        // S = 4 (128 KiB), +2 us per call; full context 4096 at S = 8 (256 KiB), 49 -> 54 us.
+        const int64_t groups_total = (int64_t)d->batch * d->num_kv_heads * row_chunks * col_splits;
+        if (d->merge == SWATTN_MERGE_FUSED && groups_total > kMergeCounters) return SWATTN_ERR_SHAPE;
+        const int64_t group_partial_bytes = std::min<int64_t>(rows_per_chunk, R) * (D / col_splits) * S * 4;
         fused = d->merge == SWATTN_MERGE_FUSED ||
-                (d->merge == SWATTN_MERGE_AUTO && chunks_total <= kMergeCounters &&
-                 chunk_partial_bytes <= kFusedMaxPartialBytes);
+                (d->merge == SWATTN_MERGE_AUTO && groups_total <= kMergeCounters &&
+                 group_partial_bytes <= kFusedMaxPartialBytes);
         if (!fused) {
             merge_grid = (rows_total + merge_rows_per_wg - 1) / merge_rows_per_wg;
             if (merge_grid > INT32_MAX) return SWATTN_ERR_SHAPE;
@@ -178,6 +193,8 @@ swattn_status_t make_plan(const swattn_desc_t* d, int32_t n_q, int32_t window, i
     out->merge_grid = (int32_t)merge_grid;
     out->fused_merge = fused;
     out->workspace_bytes = ws;
+    out->col_splits = (int32_t)col_splits;
+    out->tile_keys = (int32_t)tile_keys;
     return SWATTN_OK;
 }
 

@@ -153,41 +153,58 @@ __device__ __forceinline__ void store_out4(void* out, int64_t oi, f32x4_t v) {
 }
 
 // Fused tail of a partition workgroup that wrote its split's partials: the last of
-// the S workgroups of a (problem, KV head, row chunk) to arrive combines the S
-// partials of the chunk's rows and writes the output, so no merge kernel runs.
+// the S workgroups of a merge group combines the group's partials and writes the
+// output, so no merge kernel runs.  A merge group is one (problem, KV head, row
+// chunk, column split): its S workgroups wrote the partials of the chunk's rows and
+// the split's output columns cs * D/col_splits .. +D/col_splits, one key split
+// each, and the workgroup that counts last combines exactly those columns.
 //
-// Arrival is counted in p.counters[(b * Hkv + g) * row_chunks + rc], which must be
-// zero when the call starts; the last of the `arrivals` workgroups that write the
-// chunk's partials (its splits, times its column splits) sets it back to zero.  The partials
-// were written with device-coherent stores (store_partial4/1); every wave waits until
-// its stores have completed before the workgroup counts itself (an agent-scope atomic
-// add), and the workgroup that counts last reads the partials with device-coherent
-// loads, issued only after its count returned.  (A device-scope release fence would
-// also do, but on gfx950 it writes back the XCD's whole L2, once per wave: tens of
-// microseconds per launch.)  Every thread of every workgroup must call this: it
-// contains barriers.
+// Arrival is counted in p.counters[((b * Hkv + g) * row_chunks + rc) * col_splits
+// + cs], which must be zero when the call starts; the last of the group's S
+// workgroups sets it back to zero.  The partials were written with
+// device-coherent stores (store_partial4/1); every wave waits until its stores have
+// completed before the workgroup counts itself (an agent-scope atomic add), and the
+// workgroup that counts last reads the partials with device-coherent loads, issued
+// only after its count returned.  (A device-scope release fence would also do, but
+// on gfx950 it writes back the XCD's whole L2, once per wave: tens of microseconds
+// per launch.)  Every thread of every workgroup must call this: it contains
+// barriers.
+//
+// Why this ordering suffices: the LLVM AMDGPU memory model (AMDGPUUsage, "Memory
+// Model GFX942", which gfx950 follows) implements an agent-scope release as "wait
+// for every earlier store to complete" (s_waitcnt vmcnt(0)) plus a write-back of the
+// L2 lines that other agents' caches may not see, and an agent-scope acquire as an
+// invalidate of the L1 / non-coherent L2 lines before later loads.  Here the only
+// data that crosses workgroups is written with sc1 stores, which go past the
+// non-coherent L2 to the device-coherent level, and read with sc1 loads, which miss
+// in the non-coherent caches; so the wait for the stores is the whole release and
+// the coherent loads after the atomic's return are the whole acquire.  The atomic
+// itself is relaxed: the waits before it (stores complete, then a barrier) and the
+// control dependency after it (loads are issued only once its value returned and
+// the barrier published it) order the accesses.
 template <int D, bool OUT_F32, int NT>
-__device__ __forceinline__ void merge_if_last(const PartitionParams& p, int b, int g, int rc, int arrivals) {
+__device__ __forceinline__ void merge_if_last(const PartitionParams& p, int b, int g, int rc, int cs) {
     __shared__ int last;
     __builtin_amdgcn_s_waitcnt(0);           // this wave's partial stores are done
     __syncthreads();
     if (threadIdx.x == 0) {
-        int* c = p.counters + ((int64_t)b * p.Hkv + g) * p.row_chunks + rc;
+        int* c = p.counters + (((int64_t)b * p.Hkv + g) * p.row_chunks + rc) * p.col_splits + cs;
         const int arrived = __hip_atomic_fetch_add(c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1;
-        const bool is_last = arrived == arrivals;
+        const bool is_last = arrived == p.S;
         // every split has counted: ready for the next call
         if (is_last) __hip_atomic_store(c, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         last = is_last;
     }
     __syncthreads();
     if (!last) return;
-    constexpr int TPR = D / 4;                   // threads per row, 4 dims each
+    const int DC = D / p.col_splits;             // the group's output columns
+    const int TPR = DC / 4;                      // threads per row, 4 dims each
     const int64_t unit = (int64_t)b * p.Hkv + g;
     const int r0 = rc * p.rows_per_chunk;
     const int nr = min(p.R - r0, p.rows_per_chunk);
     for (int slot = threadIdx.x; slot < nr * TPR; slot += NT) {
         const int r = r0 + slot / TPR;
-        const int dq = (slot % TPR) * 4;
+        const int dq = cs * DC + (slot % TPR) * 4;
         const f32x4_t v = combine_splits4<D, true>(p.ws_o, p.ws_lse, unit, p.S, p.R, r, dq);
         const int i = r / p.G;
         const int h = g * p.G + (r - i * p.G);

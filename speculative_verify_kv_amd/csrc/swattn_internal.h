@@ -48,7 +48,7 @@ struct PartitionParams {
     int32_t bs_log2;      // log2(bs) when bs is a power of two, else -1
     int32_t n_q, window, R, max_ctx;
     int32_t S, rows_per_chunk, row_chunks;
-    int32_t col_splits;   // workgroups per row chunk splitting its output columns (1 or 2)
+    int32_t col_splits;   // workgroups per row chunk splitting its output columns (1, 2 or 4)
     int32_t q_dtype, kv_dtype, out_dtype;
     float scale_log2;     // scale * log2(e)
     int32_t tile_keys;    // matrix-core kernel: keys per tile, 32 or 64

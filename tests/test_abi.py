@@ -28,7 +28,7 @@ def test_library_exports_every_header_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert sw.swattn_abi_version() == sw.ABI_VERSION == 2
+    assert sw.swattn_abi_version() == sw.ABI_VERSION == 3
     for code in sw.STATUS:
         s = sw.swattn_status_str(code)
         assert s and s != "unknown status"

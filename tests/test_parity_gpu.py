@@ -603,3 +603,40 @@ def test_all_ones_values_give_one(variant, kv):
         gu.log(f"[ones] variant {variant} kv {kv} f32 {out_f32}: max |out-1| {np.abs(got - 1).max():.3e}")
         # within bfloat16 rounding: one bf16 step below 1 is 2^-8
         assert np.isfinite(got).all() and np.abs(got - 1.0).max() <= 2.0 ** -8
+
+
+# ---------------------------------------------------------------------------
+# E4M3 plain decode on 16-row chunks split four ways by columns, with splits
+# combined by the fused tail (each (row chunk, column split) group merges its own
+# columns) and by the merge kernel: identical bits, oracle parity, counters reset
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("B", [1, 8])
+def test_e4m3_decode_column_quarters_fused_merge(B):
+    w = synth.make_workload(f"e4m3dec{B}", B=B, H=8, Hkv=2, D=256, n_q=1, window=188, ctx=None, bs=16, seed=130 + B,
+                            kv_dtype="e4m3", recent=188, ctx_range=(1, 4096), max_blocks=256)
+    ref = gu.reference(w)
+    t = gu.upload(w)
+    auto, aplan = gu.run(w, t, out_f32=True, max_ctx=4096)
+    gu.log(f"[e4m3 decode] B={B} auto plan {aplan.as_dict()}")
+    gu.check(auto, ref, w.kv_dtype, True, label=f"e4m3 decode B={B} auto")
+    for S in (2, 3):
+        outs = {}
+        for merge in (sw.SWATTN_MERGE_KERNEL, sw.SWATTN_MERGE_FUSED):
+            desc = sw.make_desc(t["q"], t["k"], t["bt"], 4096, out_dtype=sw.SWATTN_F32, k_scale=t["ks"],
+                                v_scale=t["vs"], num_splits=S, merge=merge, rows_per_chunk=16, col_splits=4)
+            plan = sw.swattn_plan(desc, w.n_q, w.window)
+            assert plan.col_splits == 4 and plan.rows_per_chunk == 16 and plan.num_splits == S
+            assert plan.fused_merge == (merge == sw.SWATTN_MERGE_FUSED)
+            ws = torch.zeros(plan.workspace_bytes, dtype=torch.uint8, device=gu.DEV)
+            for rep in range(3):
+                out = torch.empty(t["q"].shape, dtype=torch.float32, device=gu.DEV)
+                sw.swattn_verify(desc, t["q"], t["k"], t["v"], t["bt"], t["ctx"], w.n_q, w.window, w.scale, out, ws,
+                                 plan.workspace_bytes, torch.cuda.current_stream().cuda_stream)
+                torch.cuda.synchronize()
+                got = out.cpu().numpy().astype(np.float64)
+                if merge in outs:
+                    assert np.array_equal(got, outs[merge]), f"S={S} merge={merge} rep {rep} not reproducible"
+                outs[merge] = got
+            assert int(ws[:sw.SWATTN_WORKSPACE_COUNTER_BYTES].count_nonzero()) == 0
+            gu.check(outs[merge], ref, w.kv_dtype, True, label=f"e4m3 decode B={B} S={S} merge={merge}")
+        assert np.array_equal(outs[sw.SWATTN_MERGE_KERNEL], outs[sw.SWATTN_MERGE_FUSED])
