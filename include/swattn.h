@@ -64,7 +64,9 @@ typedef enum {
     SWATTN_ERR_CTX = -8,          /* a ctx_len outside [n_q, min(max_ctx_len, max_blocks*block_size)] */
     SWATTN_ERR_BLOCK = -9,        /* a referenced block id outside [0, num_blocks) */
     SWATTN_ERR_HIP = -10,         /* a HIP runtime call failed */
-    SWATTN_ERR_ARG = -11          /* other invalid argument (scale not finite, bad override) */
+    SWATTN_ERR_ARG = -11,         /* other invalid argument (scale not finite, bad override) */
+    SWATTN_ERR_SCRATCH = -12      /* swattn_verify_noalloc: the plan's workspace exceeds
+                                     SWATTN_STATIC_SCRATCH_BYTES */
 } swattn_status_t;
 
 typedef enum {
@@ -321,6 +323,29 @@ swattn_status_t swattn_greedy_accept(const void* logits, swattn_dtype_t logits_d
 swattn_status_t swattn_check_inputs(const swattn_desc_t* desc, const int32_t* block_table,
                                     const int32_t* ctx_len, int32_t n_q, int32_t window,
                                     void* stream);
+
+/*
+ * swattn_verify_noalloc — swattn_verify without a workspace argument, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Arguments, layouts, semantics, results
+ * and errors are those of swattn_verify (the same plan and kernels), except that a
+ * split plan's workspace is a device array inside the library, one per GPU, of
+ * SWATTN_STATIC_SCRATCH_BYTES bytes, held until the process ends.  The call never
+ * allocates or frees (nor does anything it calls).  A plan whose workspace is larger
+ * returns SWATTN_ERR_SCRATCH before anything is enqueued (swattn_plan tells the
+ * size; num_splits or merge choices change it).  The first call on a device that
+ * needs the array also enqueues, on `stream`, a small kernel that zeroes its arrival
+ * counters; every call leaves them zero.  Calls on one GPU share its array: calls
+ * that overlap in time on one GPU (other streams or threads) race and must not be
+ * issued.
+ */
+#define SWATTN_STATIC_SCRATCH_BYTES (16u << 20)
+
+swattn_status_t swattn_verify_noalloc(const swattn_desc_t* desc,
+                                      const void* q, const void* k_cache, const void* v_cache,
+                                      const int32_t* block_table, const int32_t* ctx_len,
+                                      int32_t n_q, int32_t window, float scale,
+                                      void* out, void* stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char* swattn_status_str(swattn_status_t status);

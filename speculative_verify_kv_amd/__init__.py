@@ -6,7 +6,7 @@ kernels of ``libswattn.so``.  The functions mirror the C ABI in
 ``swattn_workspace_init``, ``swattn_verify``, ``swattn_prefill_plan``, ``swattn_prefill``,
 ``swattn_append_kv``, ``swattn_append_verify``, ``swattn_greedy_accept_workspace``,
 ``swattn_greedy_accept``, ``swattn_check_inputs``, ``swattn_status_str``,
-``swattn_abi_version``);
+``swattn_abi_version``, ``swattn_verify_noalloc``);
 ``verify`` and ``prefill`` are conveniences that fill the descriptor from torch
 tensors and run on torch's current HIP stream.  There is no CPU
 fallback: if the library is missing, loading fails with an error.
@@ -28,13 +28,15 @@ STATUS = {
     0: "SWATTN_OK", -1: "SWATTN_ERR_NULL", -2: "SWATTN_ERR_SHAPE", -3: "SWATTN_ERR_NQ",
     -4: "SWATTN_ERR_WINDOW", -5: "SWATTN_ERR_DTYPE", -6: "SWATTN_ERR_ALIGN",
     -7: "SWATTN_ERR_WORKSPACE", -8: "SWATTN_ERR_CTX", -9: "SWATTN_ERR_BLOCK",
-    -10: "SWATTN_ERR_HIP", -11: "SWATTN_ERR_ARG",
+    -10: "SWATTN_ERR_HIP", -11: "SWATTN_ERR_ARG", -12: "SWATTN_ERR_SCRATCH",
 }
+SWATTN_STATIC_SCRATCH_BYTES = 16 << 20
 
 # Symbols declared in include/swattn.h.
 EXPORTED = ("swattn_plan", "swattn_workspace_bytes", "swattn_workspace_init", "swattn_verify", "swattn_prefill_plan",
             "swattn_prefill", "swattn_append_kv", "swattn_append_verify", "swattn_greedy_accept_workspace",
-            "swattn_greedy_accept", "swattn_check_inputs", "swattn_status_str", "swattn_abi_version")
+            "swattn_greedy_accept", "swattn_check_inputs", "swattn_status_str", "swattn_abi_version",
+            "swattn_verify_noalloc")
 
 
 class SwattnError(RuntimeError):
@@ -98,6 +100,10 @@ def lib():
                                     ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                     ctypes.c_void_p]
         L.swattn_verify.restype = ctypes.c_int
+        L.swattn_verify_noalloc.argtypes = [P(swattn_desc_t), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                            ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p]
+        L.swattn_verify_noalloc.restype = ctypes.c_int
         L.swattn_prefill_plan.argtypes = L.swattn_plan.argtypes
         L.swattn_prefill_plan.restype = ctypes.c_int
         L.swattn_prefill.argtypes = L.swattn_verify.argtypes
@@ -184,6 +190,16 @@ def swattn_verify(desc, q, k_cache, v_cache, block_table, ctx_len, n_q, window, 
                              _ptr(stream))
     if check and st != 0:
         raise SwattnError(st, "swattn_verify")
+    return st
+
+
+def swattn_verify_noalloc(desc, q, k_cache, v_cache, block_table, ctx_len, n_q, window, scale, out, stream=None,
+                          check=True):
+    st = lib().swattn_verify_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                     _ptr(block_table), _ptr(ctx_len), int(n_q), int(window), float(scale),
+                                     _ptr(out), _ptr(stream))
+    if check and st != 0:
+        raise SwattnError(st, "swattn_verify_noalloc")
     return st
 
 

@@ -24,16 +24,9 @@ int dtype_bytes(int dt) { return dt == SWATTN_F32 ? 4 : (dt == SWATTN_BF16 ? 2 :
 }  // namespace swattn
 
 namespace swattn {
-namespace {
 
 // An attention call, checked and laid out (verify or prefill: they differ only in the
 // n_q cap); nothing is enqueued.
-struct AttendCall {
-    swattn_plan_t plan;
-    PartitionParams p;
-    MergeParams m;
-};
-
 swattn_status_t prepare_attend(const swattn_desc_t* d, const void* q, const void* k_cache, const void* v_cache,
                                const int32_t* block_table, const int32_t* ctx_len, int32_t n_q, int32_t window,
                                float scale, void* out, void* workspace, size_t workspace_bytes, int32_t max_nq,
@@ -140,15 +133,8 @@ swattn_status_t launch_attend(const AttendCall& call, void* stream) {
     return SWATTN_OK;
 }
 
-swattn_status_t attend(const swattn_desc_t* d, const void* q, const void* k_cache, const void* v_cache,
-                       const int32_t* block_table, const int32_t* ctx_len, int32_t n_q, int32_t window,
-                       float scale, void* out, void* workspace, size_t workspace_bytes, void* stream,
-                       int32_t max_nq) {
-    AttendCall call;
-    const swattn_status_t st = prepare_attend(d, q, k_cache, v_cache, block_table, ctx_len, n_q, window, scale,
-                                              out, workspace, workspace_bytes, max_nq, &call);
-    return st != SWATTN_OK ? st : launch_attend(call, stream);
-}
+
+namespace {
 
 // The checks and launch shape of an append call; nothing is enqueued.
 swattn_status_t prepare_append(const swattn_desc_t* d, const void* k_new, const void* v_new,
@@ -202,6 +188,17 @@ swattn_status_t prepare_append(const swattn_desc_t* d, const void* k_new, const 
 }
 
 }  // namespace
+
+swattn_status_t attend(const swattn_desc_t* d, const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_table, const int32_t* ctx_len, int32_t n_q, int32_t window,
+                       float scale, void* out, void* workspace, size_t workspace_bytes, void* stream,
+                       int32_t max_nq) {
+    AttendCall call;
+    const swattn_status_t st = prepare_attend(d, q, k_cache, v_cache, block_table, ctx_len, n_q, window, scale,
+                                              out, workspace, workspace_bytes, max_nq, &call);
+    return st != SWATTN_OK ? st : launch_attend(call, stream);
+}
+
 }  // namespace swattn
 
 extern "C" swattn_status_t swattn_verify(const swattn_desc_t* d, const void* q, const void* k_cache,

@@ -240,6 +240,8 @@ const char* swattn_status_str(swattn_status_t s) {
         case SWATTN_ERR_BLOCK: return "a block id read by some window lies outside [0, num_blocks)";
         case SWATTN_ERR_HIP: return "HIP runtime error";
         case SWATTN_ERR_ARG: return "invalid argument";
+        case SWATTN_ERR_SCRATCH:
+            return "the plan needs more workspace than the library's static scratch (SWATTN_STATIC_SCRATCH_BYTES) holds";
     }
     return "unknown status";
 }

@@ -92,6 +92,27 @@ struct AcceptParams {
 // Geometry helpers used by both the planner and the host launch code.
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+// Planning and the attention call of swattn_verify / swattn_prefill (plan.cpp, api.cpp):
+// checks, plan and launches on `stream`, with the given workspace.
+swattn_status_t make_plan(const swattn_desc_t* d, int32_t n_q, int32_t window, int32_t max_nq,
+                          swattn_plan_t* out);
+swattn_status_t attend(const swattn_desc_t* d, const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_table, const int32_t* ctx_len, int32_t n_q, int32_t window,
+                       float scale, void* out, void* workspace, size_t workspace_bytes, void* stream,
+                       int32_t max_nq);
+// The same call in two halves: every check and the launch parameters (nothing is
+// enqueued), then the launches.
+struct AttendCall {
+    swattn_plan_t plan;
+    PartitionParams p;
+    MergeParams m;
+};
+swattn_status_t prepare_attend(const swattn_desc_t* d, const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* block_table, const int32_t* ctx_len, int32_t n_q, int32_t window,
+                               float scale, void* out, void* workspace, size_t workspace_bytes, int32_t max_nq,
+                               AttendCall* call);
+swattn_status_t launch_attend(const AttendCall& call, void* stream);
+
 // Kernel launchers (defined in the .hip files).  They return a hipError_t as int.
 int launch_partition_mfma(const PartitionParams& p, int grid, void* stream);
 int launch_partition_valu(const PartitionParams& p, int grid, void* stream);
