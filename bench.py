@@ -62,6 +62,10 @@ TRAFFIC_SUMMARIES = {
     "batched_fp8": os.path.join(ROOT, "profiles", "traffic_batched_256seq_2kv_d256_e4m3_w188_nq8.txt"),
     "batched_bf16": os.path.join(ROOT, "profiles", "traffic_batched_256seq_2kv_d256_bf16_w188_nq8.txt"),
     "decode": os.path.join(ROOT, "profiles", "traffic_decode_24x2kv_d256_w188_nq1.txt"),
+    "wide_verify": os.path.join(ROOT, "profiles", "traffic_wideverify_24x2kv_d256_w188_nq64.txt"),
+    "prefill_512": os.path.join(ROOT, "profiles", "traffic_prefill_24x2kv_d256_w188_nq512.txt"),
+    "fullctx_4096": os.path.join(ROOT, "profiles", "traffic_fullctx_24x2kv_d256_w4096_ctx4096_nq8.txt"),
+    "tiny_decode": os.path.join(ROOT, "profiles", "traffic_tinydecode_1x1kv_d64_f32_w188_nq1.txt"),
 }
 KERNEL_SOURCES = ["partition_mfma.hip", "partition_valu.hip", "merge.hip", "split_merge.h", "kv_access.h",
                   "swattn_internal.h", "plan.cpp", "api.cpp"]
@@ -334,10 +338,12 @@ def main():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="default workload only: skip the batched-configuration measurements")
-    ap.add_argument("--op", default="attention", choices=["attention", "append_kv", "accept", "layer_graph"],
+    ap.add_argument("--op", default="attention",
+                    choices=["attention", "append_kv", "accept", "layer_graph", "gather_ceiling"],
                     help="attention: swattn_verify / swattn_prefill (default); append_kv: swattn_append_kv "
                          "of the workload's new rows into its cache; accept: swattn_greedy_accept; "
-                         "layer_graph: one decode step as a graph of per-layer calls")
+                         "layer_graph: one decode step as a graph of per-layer calls; gather_ceiling: "
+                         "swattn_window_gather, the workload's data movement without arithmetic")
     ap.add_argument("--vocab", type=int, default=262144, help="accept op: logits per position")
     ap.add_argument("--accept-batch", type=int, default=1, help="accept op: sequences per call")
     ap.add_argument("--calibrate-copy", type=int, default=0,
@@ -381,6 +387,16 @@ def main():
     if args.op == "layer_graph":
         run_layer_graph(args, torch, np, sw, synth, dev)
         return
+    if args.op == "gather_ceiling":
+        r = measure_attention(args.workload, args, torch, np, sw, synth, dev, gather=True)
+        line = {"metric": "data-movement floor us/call (swattn_window_gather: the verify call's algorithmic bytes "
+                          "through the same paged loads, no arithmetic)",
+                "value": r["value"], "unit": "us/call", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                "ms_per_step": round(r["value"] / 1e3, 6), "higher_is_better": False, "scaling": "weak",
+                "vs_baseline": None, "dtype": r["dtype"], "data": "synthetic", "config": r["config"],
+                "roofline": r["roofline"], "timing": r["timing"], "cpu_baseline": None}
+        print(json.dumps(line), flush=True)
+        return
 
     res = measure_attention(args.workload, args, torch, np, sw, synth, dev)
     line = {
@@ -409,10 +425,15 @@ def main():
         line["batched"] = {}
         for key in ("batched_fp8", "batched_bf16"):
             r = measure_attention(key, args, torch, np, sw, synth, dev)
+            c = measure_attention(key, args, torch, np, sw, synth, dev, gather=True)
             line["batched"][key] = {"value": r["value"], "unit": "us/call", "dtype": r["dtype"],
                                     "workload": r["config"]["workload"], "roofline": r["roofline"],
                                     "cold_eager_us_median": r["timing"]["cold_eager_us_median"],
-                                    "plan": r["plan"], "parity_spot_check": r["parity_spot_check"]}
+                                    "plan": r["plan"], "parity_spot_check": r["parity_spot_check"],
+                                    "gather_ceiling": {"value": c["value"], "unit": "us/call",
+                                                       "frac": c["roofline"]["frac"],
+                                                       "what": "swattn_window_gather on the same inputs: the same "
+                                                               "bytes and paged loads, no arithmetic"}}
             ok = ok and r["parity_spot_check"]["ok"]
     print(json.dumps(line), flush=True)
     if not ok:
@@ -420,9 +441,10 @@ def main():
         sys.exit(1)
 
 
-def measure_attention(key, args, torch, np, sw, synth, dev):
+def measure_attention(key, args, torch, np, sw, synth, dev, gather=False):
     """Cold per-call time of swattn_verify (or swattn_prefill for chunks above 64
-    positions) on a named workload, its roofline fraction and an oracle spot check."""
+    positions) on a named workload, its roofline fraction and an oracle spot check;
+    with gather=True, of swattn_window_gather on the same inputs (no spot check)."""
     import oracle
     w = synth.named_workload(key)
 
@@ -449,7 +471,10 @@ def measure_attention(key, args, torch, np, sw, synth, dev):
     stream = torch.cuda.current_stream(dev)
 
     def launch(cs):
-        call_lib(desc, q, k, v, bt, ctx, w.n_q, w.window, w.scale, out, ws, plan.workspace_bytes, cs)
+        if gather:
+            sw.swattn_window_gather(desc, q, k, v, bt, ctx, w.n_q, w.window, out, cs)
+        else:
+            call_lib(desc, q, k, v, bt, ctx, w.n_q, w.window, w.scale, out, ws, plan.workspace_bytes, cs)
 
     flush = ColdFlush(torch, dev)
     for _ in range(args.warmup):
@@ -461,7 +486,7 @@ def measure_attention(key, args, torch, np, sw, synth, dev):
     got = out.float().cpu().numpy()
     rng = np.random.default_rng(0)
     worst = 0.0
-    for b in rng.choice(w.B, size=min(3, w.B), replace=False):
+    for b in (rng.choice(w.B, size=min(3, w.B), replace=False) if not gather else []):
         ref = oracle.attend(w.q[b:b + 1], w.k_cache, w.v_cache, w.block_table[b:b + 1], w.ctx_len[b:b + 1], w.n_q,
                             w.window, w.scale, q_format=w.q_format, kv_format=w.kv_format,
                             k_scale=w.k_scale, v_scale=w.v_scale)
@@ -480,7 +505,8 @@ def measure_attention(key, args, torch, np, sw, synth, dev):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic(key),
                      "algorithmic_bytes": nbytes,
-                     "kernel": "partition" + ("" if plan.num_splits == 1 or plan.fused_merge else "+merge")},
+                     "kernel": "window_gather" if gather else
+                     "partition" + ("" if plan.num_splits == 1 or plan.fused_merge else "+merge")},
         "timing": t,
         "plan": plan.as_dict(),
         "parity_spot_check": {"ok": parity_ok, "worst_excess": worst,

@@ -347,6 +347,25 @@ swattn_status_t swattn_verify_noalloc(const swattn_desc_t* desc,
                                       int32_t n_q, int32_t window, float scale,
                                       void* out, void* stream);
 
+/*
+ * swattn_window_gather — measurement aid: the data movement of swattn_verify without
+ * its arithmetic.  For each (problem, KV head) it reads the K and V rows of the union
+ * of the n_q queries' windows through the block table (the same 16-byte global-to-LDS
+ * loads as the attention kernel, all requested at once), reads the problem's Q rows,
+ * and writes zeros over its rows of `out`: exactly the bytes counted as the verify
+ * call's algorithmic traffic, so its time is the data-movement floor of that paged
+ * layout and launch shape.  Arguments and host-side checks as swattn_verify (no
+ * workspace); `out` receives zeros.  A window of more than 1024 positions is read over
+ * its first 1024, and at most 512 query rows per KV head.  Source of the window rule:
+ * "The Fast Gemma Challenge: our verified-SOTA recipe, in full", manifest
+ * SLIDING_WINDOW, SPECULATIVE_CONFIG; "What each piece does, and why" (decode is bound
+ * by the KV cache's bandwidth).
+ */
+swattn_status_t swattn_window_gather(const swattn_desc_t* desc,
+                                     const void* q, const void* k_cache, const void* v_cache,
+                                     const int32_t* block_table, const int32_t* ctx_len,
+                                     int32_t n_q, int32_t window, void* out, void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* swattn_status_str(swattn_status_t status);
 

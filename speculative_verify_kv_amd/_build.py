@@ -19,7 +19,7 @@ LIB = os.path.join(PKG, "libswattn.so")
 ARCH = "gfx950"
 
 SOURCES = ["plan.cpp", "api.cpp", "partition_mfma.hip", "partition_valu.hip", "merge.hip", "kv_append.hip",
-           "accept.hip", "noalloc.hip"]
+           "accept.hip", "noalloc.hip", "gather.hip"]
 
 # hipcc's host pass does not know this target feature and says so; harmless.
 # It keeps the device compiler from forming packed-fp32 instructions.

@@ -640,3 +640,18 @@ def test_e4m3_decode_column_quarters_fused_merge(B):
             assert int(ws[:sw.SWATTN_WORKSPACE_COUNTER_BYTES].count_nonzero()) == 0
             gu.check(outs[merge], ref, w.kv_dtype, True, label=f"e4m3 decode B={B} S={S} merge={merge}")
         assert np.array_equal(outs[sw.SWATTN_MERGE_KERNEL], outs[sw.SWATTN_MERGE_FUSED])
+
+
+# ---------------------------------------------------------------------------
+# the measurement aid: the verify call's data movement without arithmetic
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("key", ["batched_fp8", "verify", "tiny_decode"])
+def test_window_gather_moves_the_data_and_writes_zeros(key):
+    w, _ = gu.named(key)
+    t = gu.upload(w)
+    out = torch.full(t["q"].shape, 7.0, dtype=torch.float32 if w.q_dtype == "f32" else torch.bfloat16, device=gu.DEV)
+    desc = sw.make_desc(t["q"], t["k"], t["bt"], int(w.ctx_len.max()), k_scale=t["ks"], v_scale=t["vs"])
+    sw.swattn_window_gather(desc, t["q"], t["k"], t["v"], t["bt"], t["ctx"], w.n_q, w.window, out,
+                            torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert int(out.count_nonzero()) == 0
