@@ -108,7 +108,8 @@ typedef struct {
     /* Tuning overrides of the matrix-core launch (0: library chooses).  They force a
      * geometry; SWATTN_ERR_ARG when the plan is not the matrix-core variant or the value
      * is not offered for this shape. */
-    int32_t rows_per_chunk;       /* 16 (head_dim 256 only) or 32 query rows per workgroup */
+    int32_t rows_per_chunk;       /* 16, 32 or 64 query rows per workgroup (16 and 64: head_dim
+                                     256 only; 64: bfloat16 caches, no column split) */
     int32_t col_splits;           /* 1, 2 or 4 workgroups per row chunk, each with D/col_splits
                                      output columns (head_dim 256 only) */
 } swattn_desc_t;

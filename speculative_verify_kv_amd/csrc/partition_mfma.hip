@@ -83,10 +83,13 @@ struct Geo {
     static_assert(kCprV >= 4 && kNiV * 1024 == kTileBV, "V tile geometry");
     static constexpr int kStageB = kTileB + kTileBV;
     // Q rows of the chunk, staged once per workgroup in LDS (bfloat16, kRows x D):
-    // every compute wave reads its Q^T operand from there.
+    // every compute wave reads its Q^T operand from there.  64-row chunks with 32-key
+    // tiles do without: each of their four waves owns one row block and loads its Q^T
+    // operand straight into registers.
+    static constexpr bool kQLds = RB != 4 || KT == 64;
     static constexpr int kRowQ = D * 2;
     static constexpr int kCprQ = kRowQ / 16;
-    static constexpr int kQB = 16 * RB * kRowQ;
+    static constexpr int kQB = kQLds ? 16 * RB * kRowQ : 0;
     static constexpr int kNiQ = kQB / 1024;                 // load instructions of the Q rows
     static_assert(kNiQ * 1024 == kQB, "Q geometry");
     // Stages of the K/V ring (the ring plus < 14 KiB of tables per workgroup, 160 KiB
@@ -100,20 +103,24 @@ struct Geo {
     // two waves; otherwise it has 4 waves.  Either way a SIMD runs two waves, so each
     // may hold 256 registers.
     static constexpr int kBlocks = 2 * (kNS * kStageB + 14 * 1024) <= 160 * 1024 ? 2 : 1;
-    // Where two workgroups share a CU, the prologue leaves the last ring stage free
-    // (its tile goes out with tile 0's scores): Q is staged there.  Otherwise it has a
-    // region of its own.
-    static constexpr bool kQAlias = kBlocks == 2;
+    // Where two workgroups share a CU, and in 64-row chunks (whose 32 KiB of Q rows would
+    // not fit beside the ring), the prologue leaves the last ring stage free (its tile goes
+    // out with tile 0's scores): Q is staged there.  Otherwise it has a region of its own.
+    static constexpr bool kQAlias = kQLds && (kBlocks == 2 || RB == 4);
     static_assert(!kQAlias || kTileB >= kQB, "Q fits the K part of a ring stage");
     static_assert(kQAlias || kNS * kStageB + 14 * 1024 + kQB <= 160 * 1024, "one workgroup's LDS");
     // column sets: 64-key tiles split them only where one workgroup fills the CU;
-    // 32-key tiles always split them in two (their waves do not split the keys)
-    static constexpr int kND = kSplitKeys ? (kBlocks == 2 ? 1 : 2) : 2;
-    // row blocks of 16 query rows per workgroup: 2, or 1 for launches that leave most
-    // CUs idle (two workgroups then share a 32-row chunk's keys, each with half the work)
-    static_assert(RB == 2 || (RB == 1 && KT == 64), "16-row chunks with 64-key tiles only");
+    // 32-key tiles split them in two (their waves do not split the keys), except in
+    // 64-row chunks, whose four waves take one row block each
+    static constexpr int kND = RB == 4 ? 1 : (kSplitKeys ? (kBlocks == 2 ? 1 : 2) : 2);
+    // row blocks of 16 query rows per workgroup: 2; 1 for launches that leave most CUs
+    // idle (two workgroups then share a 32-row chunk's keys, each with half the work); 4
+    // for chunks of many query rows, so that every K/V tile serves 64 rows
+    static_assert(RB == 2 || (RB == 1 && KT == 64) || (RB == 4 && CS == 1 && !FP8),
+                  "16-row chunks with 64-key tiles; 64-row chunks for bfloat16 caches");
     static constexpr int kRows = 16 * RB;
-    static constexpr int kNWc = kSplitKeys ? 2 * RB * kND : 4;   // compute waves: row blocks x key halves x column sets
+    static constexpr int kLgRB = RB == 4 ? 2 : RB - 1;      // log2 of the row blocks
+    static constexpr int kNWc = kSplitKeys ? 2 * RB * kND : RB * kND;   // compute waves: row blocks x key halves x column sets
     // 16-row workgroups (one per CU for bfloat16) add as many loader waves, which take
     // their share of every tile's loads and do no arithmetic: a workgroup's load rate
     // grows with the number of waves issuing its loads (a memory-only probe of the
@@ -234,11 +241,12 @@ __global__ __launch_bounds__((Geo<D, FP8, KT, RB, CS>::kNT), (Geo<D, FP8, KT, RB
     __shared__ __attribute__((aligned(16))) const unsigned char* kptr[kMfmaMaxKeys];
     __shared__ __attribute__((aligned(16))) const unsigned char* vptr[kMfmaMaxKeys];
     __shared__ int tbl[NT];
-    __shared__ float xstat[2][2][2][16];         // [rb][kh][m, l][row]
+    __shared__ float xstat[RB == 4 ? 4 : 2][2][2][16];   // [rb][kh][m, l][row]
     // the chunk's Q rows: the K part of the last ring stage where two workgroups share a
-    // CU, else a region of their own (in the K stages' array, past the ring)
-    __shared__ __attribute__((aligned(16))) unsigned char qst[G::kQAlias ? 16 : G::kQB];
-    static_assert(2 * 2 * 16 * (D / 2) * 4 <= (int)sizeof(kst), "merge exchange fits in the K stages");
+    // CU, else a region of their own (none for 64-row chunks: their Q goes to registers)
+    __shared__ __attribute__((aligned(16))) unsigned char qst[G::kQAlias || !G::kQLds ? 16 : G::kQB];
+    static_assert(!G::kSplitKeys || RB * 2 * G::kND * 16 * (D / G::kCS / G::kND / 2) * 4 <= (int)sizeof(kst),
+                  "merge exchange fits in the K stages");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -247,10 +255,10 @@ __global__ __launch_bounds__((Geo<D, FP8, KT, RB, CS>::kNT), (Geo<D, FP8, KT, RB
     const int cw = loader ? 0 : wave;            // compute-wave index (loaders mirror wave 0)
     const int l16 = lane & 15;
     const int q4 = lane >> 4;
-    const int rb = RB == 2 ? cw & 1 : 0;        // 16-row block
+    const int rb = RB == 4 ? cw & 3 : (RB == 2 ? cw & 1 : 0);   // 16-row block
     // key half of every tile (64-key tiles) and column set
-    const int kh = G::kSplitKeys ? (cw >> (RB - 1)) & 1 : 0;
-    const int dh = G::kSplitKeys ? cw >> RB : (cw >> 1) & 1;
+    const int kh = G::kSplitKeys ? (cw >> G::kLgRB) & 1 : 0;
+    const int dh = G::kSplitKeys ? cw >> (G::kLgRB + 1) : (RB == 4 ? 0 : (cw >> 1) & 1);
 
     // grid (B * Hkv, row chunks x column splits, splits)
     const int s = blockIdx.z;
@@ -293,6 +301,18 @@ __global__ __launch_bounds__((Geo<D, FP8, KT, RB, CS>::kNT), (Geo<D, FP8, KT, RB
     const int qrow = rc * G::kRows + rb * 16 + l16;
     const bool qvalid = qrow < p.R;
     const int qi = qvalid ? qrow / p.G : 0;
+    // Q^T operand of this lane: row rb*16 + l16 of the chunk, dims ks*32 + q4*8 .. +7.
+    // 64-row chunks load it here, beside the ctx_len and block-table round trip (a row
+    // past R loads a valid row); the others read it from the Q rows in LDS below.
+    uint4 qreg[KS];
+    if constexpr (!G::kQLds) {
+        const int r = min(qrow, p.R - 1);
+        const int i = r / p.G, h = g * p.G + (r - i * p.G);
+        const uint4* qp = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p.q) +
+                                                         (((int64_t)b * p.n_q + i) * p.H + h) * D + q4 * 8);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qreg[ks] = qp[ks * 4];
+    }
     float scale_log2 = p.scale_log2;
     float out_scale = 1.0f;
     if constexpr (FP8) {
@@ -400,18 +420,17 @@ __global__ __launch_bounds__((Geo<D, FP8, KT, RB, CS>::kNT), (Geo<D, FP8, KT, RB
     // The first tiles go out together, one per stage: all NS where one workgroup has
     // the CU, NS-1 where two share it (tile NS-1 then goes out with tile 0's scores:
     // a wave whose loads stall at issue reaches its first tile sooner; batched E4M3,
-    // 512 workgroups: 21.4 -> 20.2 us).
-    constexpr int kPro = G::kBlocks == 2 ? NS - 1 : NS;
+    // 512 workgroups: 21.4 -> 20.2 us) or where Q sits in the last stage.
+    constexpr int kPro = (G::kQAlias || G::kBlocks == 2) ? NS - 1 : NS;
 #pragma unroll
     for (int t = 0; t < kPro; ++t)
         if (t < ntiles) issue_range(t, 0, SH);
 
-    // Q^T operand of this lane: row rb*16 + l16, dims ks*32 + q4*8 .. +7, from the Q
-    // rows in LDS (landed before the block-table barrier).  The barrier of tile 0 orders
-    // these reads before tile NS-1 goes into the stage that Q may share.
-    uint4 qreg[KS];
-    if (ntiles > 0) {
-        if (!loader) {
+    // The Q^T operands from the Q rows in LDS (landed before the block-table barrier).
+    // The barrier of tile 0 orders these reads before tile NS-1 goes into the stage that
+    // Q may share.
+    if constexpr (G::kQLds) {
+        if (ntiles > 0 && !loader) {
             const int row = rb * 16 + l16;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
@@ -793,6 +812,13 @@ int launch_d(const PartitionParams& p, int grid, hipStream_t st) {
     if constexpr (D == 256) {
         if (p.tile_keys == 32 && p.kv_dtype == SWATTN_BF16 && p.rows_per_chunk == 32 && p.col_splits == 1)
             return launch_dk<D, 32, false, 2>(p, grid, st);
+        // 64-row chunks (bfloat16 caches): 64-key tiles at one workgroup per CU while the
+        // grid fits the CUs, else 32-key tiles at two per CU
+        if (p.rows_per_chunk == 64) {
+            if (p.kv_dtype != SWATTN_BF16 || p.col_splits != 1) return (int)hipErrorInvalidValue;
+            return p.tile_keys == 64 ? launch_dk<D, 64, false, 4>(p, grid, st)
+                                     : launch_dk<D, 32, false, 4>(p, grid, st);
+        }
         if (p.tile_keys != 64) return (int)hipErrorInvalidValue;
         // 16-row chunks, and 32-row chunks split by columns: bfloat16 and E4M3 caches
         if (p.rows_per_chunk == 16)

@@ -21,6 +21,9 @@ constexpr bool kMfmaHalfRows = true;    // 16-row chunks for launches that leave
 // but the call is bound by its chain of key loads, which that kernel issues a whole
 // tile at a time (24-layer decode, n_q 1: 27.5 -> 11.0 us; one layer: 27 -> 8.9 us).
 constexpr bool kMfmaSmallRows = true;
+// 64-row chunks (32-key tiles) for bfloat16 caches of head_dim 256 with at least 64
+// query rows per KV head: every K/V tile then serves twice the rows of a 32-row chunk.
+constexpr bool kMfmaTallRows = true;
 constexpr int64_t kFusedMaxPartialBytes = 16 * 1024;   // automatic fused merge up to this much per chunk
 
 bool dtype_in(int v, std::initializer_list<int> ok) {
@@ -93,8 +96,11 @@ swattn_status_t make_plan(const swattn_desc_t* d, int32_t n_q, int32_t window, i
     const bool forced_geo = d->rows_per_chunk != 0 || d->col_splits != 0;
     if (forced_geo) {
         if (variant != SWATTN_VARIANT_MFMA) return SWATTN_ERR_ARG;
-        if (!dtype_in(d->rows_per_chunk, {0, 16, 32}) || !dtype_in(d->col_splits, {0, 1, 2, 4})) return SWATTN_ERR_ARG;
-        if ((d->rows_per_chunk == 16 || d->col_splits > 1) && d->head_dim != 256) return SWATTN_ERR_ARG;
+        if (!dtype_in(d->rows_per_chunk, {0, 16, 32, 64}) || !dtype_in(d->col_splits, {0, 1, 2, 4})) return SWATTN_ERR_ARG;
+        if ((d->rows_per_chunk == 16 || d->rows_per_chunk == 64 || d->col_splits > 1) && d->head_dim != 256)
+            return SWATTN_ERR_ARG;
+        // 64-row chunks: bfloat16 caches, one workgroup per chunk
+        if (d->rows_per_chunk == 64 && (d->kv_dtype != SWATTN_BF16 || d->col_splits > 1)) return SWATTN_ERR_ARG;
     }
     if (variant == SWATTN_VARIANT_MFMA) {
         rows_per_chunk = kMfmaRows;
@@ -132,15 +138,27 @@ swattn_status_t make_plan(const swattn_desc_t* d, int32_t n_q, int32_t window, i
         if (kMfmaHalfRows && d->head_dim == 256 && g16 <= kComputeUnits) {
             rows_per_chunk = kMfmaRows / 2;
             col_splits = 4 * g16 <= kComputeUnits ? 4 : (2 * g16 <= kComputeUnits ? 2 : 1);
+        } else if (kMfmaTallRows && d->head_dim == 256 && d->kv_dtype == SWATTN_BF16 && R >= 2 * kMfmaRows) {
+            rows_per_chunk = 2 * kMfmaRows;
         }
         if (d->rows_per_chunk != 0) rows_per_chunk = d->rows_per_chunk;
         if (d->col_splits != 0) col_splits = d->col_splits;
+        if (rows_per_chunk == 64) col_splits = 1;
+        // A taller chunk scans a longer union of windows: keep each split within the
+        // workgroup's cache-row table.
+        if (rows_per_chunk > kMfmaRows) {
+            const int64_t qpc_t = std::min<int64_t>(n_q, (rows_per_chunk - 1) / G + 2);
+            const int64_t U_t = std::min<int64_t>(d->max_ctx_len, (int64_t)window + qpc_t - 1);
+            S = std::max(S, (U_t + kMfmaMaxKeys - 1) / kMfmaMaxKeys);
+        }
         // Tiles of 64 keys, or 32 where a 64-key workgroup needs a CU's whole LDS (bfloat16
         // cache, head_dim 256, 32-row chunks, no column split) and there are more
         // workgroups than CUs: 32-key tiles let two workgroups share a CU.
         const bool one_per_cu = d->kv_dtype == SWATTN_BF16 && d->head_dim == 256;
         const int64_t wgs = (int64_t)d->batch * d->num_kv_heads * ((R + rows_per_chunk - 1) / rows_per_chunk) * S;
-        tile_keys = (one_per_cu && rows_per_chunk == kMfmaRows && col_splits == 1 && wgs > kComputeUnits) ? 32 : 64;
+        // 64-row chunks: 64-key tiles (eight waves, one workgroup per CU) while the grid
+        // fits the CUs, else 32-key tiles (four waves, two workgroups per CU)
+        tile_keys = (one_per_cu && rows_per_chunk >= kMfmaRows && col_splits == 1 && wgs > kComputeUnits) ? 32 : 64;
     } else {
         rows_per_chunk = kValuRowsPerChunk;
         const int64_t row_chunks = (R + rows_per_chunk - 1) / rows_per_chunk;

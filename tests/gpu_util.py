@@ -53,14 +53,16 @@ def upload(w):
     return t
 
 
-def run(w, t=None, out_f32=False, num_splits=0, variant=0, max_ctx=None, prefill=False, merge=0, workspace=None):
+def run(w, t=None, out_f32=False, num_splits=0, variant=0, max_ctx=None, prefill=False, merge=0, workspace=None,
+        rows_per_chunk=0, col_splits=0):
     """One swattn_verify (or swattn_prefill) call; returns (float64 numpy output, plan)."""
     t = upload(w) if t is None else t
     mc = int(w.ctx_len.max()) if max_ctx is None else max_ctx
     out, plan = sw.verify(t["q"], t["k"], t["v"], t["bt"], t["ctx"], w.n_q, w.window, w.scale,
                           max_ctx_len=mc, out_dtype=sw.SWATTN_F32 if out_f32 else None,
                           k_scale=t["ks"], v_scale=t["vs"], num_splits=num_splits, variant=variant,
-                          prefill=prefill, merge=merge, workspace=workspace)
+                          prefill=prefill, merge=merge, workspace=workspace, rows_per_chunk=rows_per_chunk,
+                          col_splits=col_splits)
     torch.cuda.synchronize()
     return out.float().cpu().numpy().astype(np.float64), plan
 

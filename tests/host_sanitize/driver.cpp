@@ -39,7 +39,8 @@ int launch_partition_mfma(const PartitionParams& p, int grid, void*) {
     g_rec.p = p;
     g_rec.grid = grid;
     CHECK(grid == p.B * p.Hkv * p.row_chunks * p.col_splits * p.S);
-    CHECK(p.rows_per_chunk == 16 || p.rows_per_chunk == 32);
+    CHECK(p.rows_per_chunk == 16 || p.rows_per_chunk == 32 || p.rows_per_chunk == 64);
+    if (p.rows_per_chunk == 64) CHECK(p.col_splits == 1 && p.kv_dtype == SWATTN_BF16);
     CHECK(p.col_splits == 1 || p.col_splits == 2 || p.col_splits == 4);
     CHECK(p.tile_keys == 32 || p.tile_keys == 64);
     CHECK(p.row_chunks == (p.R + p.rows_per_chunk - 1) / p.rows_per_chunk);

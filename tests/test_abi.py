@@ -75,12 +75,34 @@ def status(d, n_q=8, window=188):
     (dict(num_splits=-1), 8, 188, "SWATTN_ERR_ARG"),
     (dict(merge=3), 8, 188, "SWATTN_ERR_ARG"),
     (dict(merge=-1), 8, 188, "SWATTN_ERR_ARG"),
+    # chunk-geometry overrides: 16 / 64-row chunks and column splits need head_dim 256;
+    # 64-row chunks are for bfloat16 caches and take no column split
+    (dict(rows_per_chunk=48), 8, 188, "SWATTN_ERR_ARG"),
+    (dict(col_splits=3), 8, 188, "SWATTN_ERR_ARG"),
+    (dict(rows_per_chunk=16, head_dim=128), 8, 188, "SWATTN_ERR_ARG"),
+    (dict(rows_per_chunk=64, head_dim=128), 8, 188, "SWATTN_ERR_ARG"),
+    (dict(rows_per_chunk=64, col_splits=2), 8, 188, "SWATTN_ERR_ARG"),
+    (dict(rows_per_chunk=64, kv_dtype=sw.SWATTN_FP8_E4M3, k_scale=16, v_scale=32), 8, 188, "SWATTN_ERR_ARG"),
+    (dict(rows_per_chunk=64, variant=sw.SWATTN_VARIANT_VALU), 8, 188, "SWATTN_ERR_ARG"),
+    (dict(rows_per_chunk=64), 8, 188, "SWATTN_OK"),
+    (dict(rows_per_chunk=16, col_splits=4), 8, 188, "SWATTN_OK"),
     (dict(), 8, 188, "SWATTN_OK"),
     (dict(), 64, 188, "SWATTN_OK"),
     (dict(), 1, 2 ** 31 - 1, "SWATTN_OK"),
 ])
 def test_plan_validation(kw, n_q, window, expect):
     assert status(desc(**kw), n_q, window) == expect
+
+
+def test_tall_chunks_keep_each_split_within_the_key_table():
+    # 16 queries x 4 heads in one 64-row chunk scan W + 15 keys: past 512 at W = 500,
+    # so the 64-row plan splits in two where 32-row chunks (W + 7 keys) need none (1024
+    # units fill the CUs: no split for idle CUs)
+    p = sw.swattn_plan(desc(batch=256), 16, 500)
+    assert p.rows_per_chunk == 64 and p.num_splits == 2 and p.tile_keys == 32
+    p = sw.swattn_plan(desc(batch=256, rows_per_chunk=32), 16, 500)
+    assert p.rows_per_chunk == 32 and p.num_splits == 1
+    assert sw.swattn_plan(desc(batch=256), 16, 497).num_splits == 1
 
 
 def test_plan_null_pointers():
@@ -141,8 +163,15 @@ def test_plan_variants_and_workspace():
     # float32 data -> vector ALU whatever the row count
     p = sw.swattn_plan(desc(q_dtype=sw.SWATTN_F32, kv_dtype=sw.SWATTN_F32), 64, 188)
     assert p.variant == sw.SWATTN_VARIANT_VALU and p.row_chunks == 64 * 4 // 8
-    # 64 queries x 4 = 256 rows -> eight 32-row chunks
+    # 64 queries x 4 = 256 rows -> four 64-row chunks (bfloat16 caches),
+    # eight 32-row chunks for E4M3 caches
     p = sw.swattn_plan(desc(), 64, 188)
+    assert p.rows_per_chunk == 64 and p.row_chunks == 4 and p.col_splits == 1
+    # 192 workgroups fit the CUs: 64-key tiles (one workgroup of eight waves per CU);
+    # beyond the CUs, 32-key tiles (two workgroups of four waves per CU)
+    assert p.tile_keys == 64 and p.grid == 192
+    assert sw.swattn_plan(desc(batch=40), 64, 188).tile_keys == 32
+    p = sw.swattn_plan(desc(kv_dtype=sw.SWATTN_FP8_E4M3, k_scale=16, v_scale=32), 64, 188)
     assert p.rows_per_chunk == 32 and p.row_chunks == 8
     # forced split count is honoured (within the chunk count), S = 1 needs no workspace
     p = sw.swattn_plan(desc(num_splits=1), 8, 188)
@@ -164,9 +193,9 @@ def test_prefill_plan_caps_and_per_chunk_keys():
     assert sw.swattn_plan(desc(), 65, 188, check=False)[0] == -3
     assert sw.swattn_prefill_plan(desc(), 65, 188).variant == sw.SWATTN_VARIANT_MFMA
     assert sw.swattn_prefill_plan(desc(), 513, 188, check=False)[0] == -3
-    # a 32-row chunk of GQA-4 rows spans at most 9 queries: 188 + 8 keys, one split
+    # a 64-row chunk of GQA-4 rows spans at most 17 queries: 188 + 16 keys, one split
     p = sw.swattn_prefill_plan(desc(), 512, 188)
-    assert p.num_splits == 1 and p.row_chunks == 64 and p.workspace_bytes == 0
+    assert p.num_splits == 1 and p.row_chunks == 32 and p.rows_per_chunk == 64 and p.workspace_bytes == 0
     # full-context prefill: ceil(min(4096, 4096 + 8) / 512) = 8 splits
     p = sw.swattn_prefill_plan(desc(), 512, 4096)
     assert p.num_splits == 8 and p.merge_grid > 0
@@ -201,9 +230,10 @@ def test_sixteen_row_chunks_only_while_the_grid_fits_the_cus():
     # full context (48 units x 4 or 8 splits) already fills the CUs: 32-row chunks
     assert sw.swattn_plan(desc(max_ctx_len=1024), 8, 4096).rows_per_chunk == 32
     assert sw.swattn_plan(desc(), 8, 4096).rows_per_chunk == 32
-    # 64 queries (8 chunks per KV head, 384 units) and head_dim 128: 32-row chunks
-    assert sw.swattn_plan(desc(), 64, 188).rows_per_chunk == 32
+    # 64 queries: 64-row chunks; head_dim 128: 32-row chunks
+    assert sw.swattn_plan(desc(), 64, 188).rows_per_chunk == 64
     assert sw.swattn_plan(desc(head_dim=128), 8, 188).rows_per_chunk == 32
+    assert sw.swattn_plan(desc(head_dim=128), 64, 188).rows_per_chunk == 32
     # the batched workload (512 units) keeps 32-row chunks
     assert sw.swattn_plan(desc(batch=256), 8, 188).rows_per_chunk == 32
 

@@ -342,7 +342,9 @@ def test_many_rows_per_kv_head(k):
     t = gu.upload(w)
     gu.log(f"[many rows] case {k} kv {kv}")
     got, plan = gu.run(w, t, out_f32=True)
-    assert plan.rows_per_chunk == 32 and plan.num_splits == 1 and plan.variant == sw.SWATTN_VARIANT_MFMA, \
+    # bfloat16 caches with 64 rows or more per KV head take 64-row chunks
+    rows = 64 if kv == "bf16" and w.n_q * (w.H // w.Hkv) >= 64 else 32
+    assert plan.rows_per_chunk == rows and plan.num_splits == 1 and plan.variant == sw.SWATTN_VARIANT_MFMA, \
         plan.as_dict()
     gu.check(got, ref, w.kv_dtype, True, label=f"manyrows{k}")
     got16, _ = gu.run(w, t, out_f32=False)
@@ -367,6 +369,47 @@ def test_many_units_32_key_tiles(S):
             first = got
     again, _ = gu.run(w, t=t, out_f32=True, num_splits=S)
     assert np.array_equal(first, again)
+
+
+# ---------------------------------------------------------------------------
+# 64-row chunks (bfloat16 caches, head_dim 256, Q^T loaded into registers; 64-key
+# tiles and eight waves while the grid fits the CUs, else 32-key tiles and four waves):
+# forced on shapes that span a ragged last chunk, a chunk with empty row blocks, GQA 1,
+# 4 and 8, split launches with either merge, and short contexts with narrow windows
+# ---------------------------------------------------------------------------
+TALL = [
+    dict(B=3, H=8, Hkv=2, n_q=64, window=188, ctx_range=(64, 4096), S=0, merge=0),    # 256 rows, 4 chunks
+    dict(B=5, H=8, Hkv=2, n_q=17, window=100, ctx_range=(17, 700), S=0, merge=0),     # 68 rows: 64 + 4
+    dict(B=7, H=8, Hkv=2, n_q=8, window=188, ctx_range=(8, 2000), S=0, merge=0),      # 32 rows of 64
+    dict(B=4, H=16, Hkv=2, n_q=8, window=7, ctx_range=(8, 300), S=0, merge=0),        # G 8, 64 rows
+    dict(B=2, H=2, Hkv=2, n_q=64, window=300, ctx_range=(64, 1200), S=0, merge=0),    # G 1: W + 63 keys
+    dict(B=3, H=8, Hkv=2, n_q=40, window=600, ctx_range=(40, 3000), S=3, merge=sw.SWATTN_MERGE_FUSED),
+    dict(B=3, H=8, Hkv=2, n_q=40, window=600, ctx_range=(40, 3000), S=3, merge=sw.SWATTN_MERGE_KERNEL),
+    # more chunks than CUs: 32-key tiles, two workgroups per CU (the launches above fit
+    # the CUs and take 64-key tiles)
+    dict(B=160, H=8, Hkv=2, n_q=17, window=60, ctx_range=(17, 400), S=0, merge=0),    # 640 workgroups
+]
+
+
+@pytest.mark.parametrize("k", range(len(TALL)))
+def test_sixty_four_row_chunks(k):
+    c = dict(TALL[k])
+    S, merge = c.pop("S"), c.pop("merge")
+    w = synth.make_workload(f"tall{k}", D=256, bs=16, seed=130 + k, ctx=None, kv_dtype=synth.workloads.BF16,
+                            max_blocks=256, **c)
+    ref = gu.reference(w)
+    t = gu.upload(w)
+    gu.log(f"[64-row chunks] case {k}: {TALL[k]}")
+    for out_f32 in (True, False):
+        got, plan = gu.run(w, t, out_f32=out_f32, num_splits=S, merge=merge, rows_per_chunk=64)
+        assert plan.rows_per_chunk == 64 and plan.col_splits == 1, plan.as_dict()
+        assert plan.tile_keys == (64 if plan.grid <= 256 else 32), plan.as_dict()
+        if S:
+            assert plan.num_splits == S and plan.fused_merge == (merge == sw.SWATTN_MERGE_FUSED), plan.as_dict()
+        gu.check(got, ref, w.kv_dtype, out_f32, label=f"tall{k} f32={out_f32}")
+        if out_f32:
+            again, _ = gu.run(w, t, out_f32=True, num_splits=S, merge=merge, rows_per_chunk=64)
+            assert np.array_equal(got, again)
 
 
 # ---------------------------------------------------------------------------
