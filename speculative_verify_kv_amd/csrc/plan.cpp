@@ -116,11 +116,19 @@ swattn_status_t make_plan(const swattn_desc_t* d, int32_t n_q, int32_t window, i
             // (one layer of plain decode: 9.5 -> 7.3 us).  Behind a merge kernel the
             // split costs more than it saves (the 24-layer step of per-layer verify
             // calls: 298 us at S = 4, 289 us at S = 1).
-            S = clamp64((U + 63) / 64, s_min, 8);
-            const bool half = kMfmaHalfRows && d->head_dim == 256 &&
-                              (int64_t)d->batch * d->num_kv_heads * ((R + 15) / 16) * S <= kComputeUnits;
+            // Keys are counted over the union of the chunk that will run (16 rows where
+            // they fit), and the partials per merge group, whose columns the chunk's
+            // column splits share (one layer of the verify step: 16-row chunks split four
+            // ways by columns, S = 3, 4 KiB per group: 8.45 -> 7.97 us).
+            const bool half16 = kMfmaHalfRows && d->head_dim == 256;
+            const int64_t qpc16 = std::min<int64_t>(n_q, (kMfmaRows / 2 - 1) / G + 2);
+            const int64_t U_c = half16 ? std::min<int64_t>(d->max_ctx_len, (int64_t)window + qpc16 - 1) : U;
+            S = clamp64((U_c + 63) / 64, s_min, 8);
+            const int64_t g16s = (int64_t)d->batch * d->num_kv_heads * ((R + 15) / 16) * S;
+            const bool half = half16 && g16s <= kComputeUnits;
+            const int64_t cs_c = !half ? 1 : (4 * g16s <= kComputeUnits ? 4 : (2 * g16s <= kComputeUnits ? 2 : 1));
             const int64_t chunk_rows = std::min<int64_t>(R, half ? kMfmaRows / 2 : kMfmaRows);
-            if (chunk_rows * D * S * 4 > kFusedMaxPartialBytes) S = s_min;
+            if (chunk_rows * (D / cs_c) * S * 4 > kFusedMaxPartialBytes) S = s_min;
         }
         else
             // While the launch leaves CUs idle, split long key ranges further, down to

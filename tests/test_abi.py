@@ -206,10 +206,10 @@ def test_sixteen_row_chunks_only_while_the_grid_fits_the_cus():
     # it fits the CUs 2 or 4 times over.  Verify step: 96 16-row chunks, twice over 192
     p = sw.swattn_plan(desc(), 8, 188)
     assert p.rows_per_chunk == 16 and p.grid == 96 * 2
-    # one layer (2 units, no split): 4 16-row chunks, four column quarters each; with 4
-    # splits forced, 16 chunk-splits, four quarters each
+    # one layer (2 units): 4 16-row chunks, four column quarters each, one split per 64-key
+    # tile of the chunk's 192 keys (3); with 4 splits forced, 16 chunk-splits, four quarters
     p = sw.swattn_plan(desc(batch=1), 8, 188)
-    assert p.rows_per_chunk == 16 and p.num_splits == 1 and p.grid == 4 * 4
+    assert p.rows_per_chunk == 16 and p.num_splits == 3 and p.col_splits == 4 and p.grid == 4 * 4 * 3
     p = sw.swattn_plan(desc(batch=1, num_splits=4), 8, 188)
     assert p.rows_per_chunk == 16 and p.num_splits == 4 and p.grid == 16 * 4
     # plain decode: one 16-row chunk per KV head.  24 layers: 48, four times over 192;
@@ -243,10 +243,15 @@ def test_small_launches_split_per_tile():
     # partials (4 rows x 256 x 4 splits x 4 B = 16 KiB) the last workgroup merges
     p = sw.swattn_plan(desc(batch=1), 1, 188)
     assert p.variant == sw.SWATTN_VARIANT_MFMA and p.num_splits == 3 and p.fused_merge == 1
-    # one layer of the verify step: 16-row partials of 4 splits (64 KiB) would need the
-    # merge kernel -> no split
+    # one layer of the verify step: a 16-row chunk scans 188 + 4 keys -> 3 splits; a merge
+    # group is a chunk's column quarter, 16 rows x 64 columns x 3 splits x 4 B = 12 KiB,
+    # which its last workgroup merges
     p = sw.swattn_plan(desc(batch=1), 8, 188)
-    assert p.variant == sw.SWATTN_VARIANT_MFMA and p.num_splits == 1 and p.merge_grid == 0
+    assert p.variant == sw.SWATTN_VARIANT_MFMA and p.num_splits == 3 and p.fused_merge == 1
+    assert p.col_splits == 4 and p.merge_grid == 0
+    # head_dim 128 (no 16-row chunks): 32-row partials of 4 splits, 64 KiB -> no split
+    p = sw.swattn_plan(desc(batch=1, head_dim=128), 8, 188)
+    assert p.num_splits == 1 and p.rows_per_chunk == 32
     # 24 layers stacked: 48 units, no split
     assert sw.swattn_plan(desc(batch=24), 8, 188).num_splits == 1
     # head_dim 64 keeps 32-row chunks: 32 rows x 64 x 4 splits x 4 B = 32 KiB -> no split;

@@ -131,17 +131,20 @@ def test_append_verify_bad_inputs_match_the_two_calls():
     t["bt"] = torch.from_numpy(bt).to(gu.DEV)
     knd, vnd = _dev_rows(kn, new), _dev_rows(vn, new)
     desc = sw.make_desc(t["q"], t["k"], t["bt"], 4096, out_dtype=sw.SWATTN_F32)
+    plan = sw.swattn_plan(desc, 8, w.window)
     stream = torch.cuda.current_stream().cuda_stream
     outs, caches = [], []
     for fused in (True, False):
         k, v = t["k"].clone(), t["v"].clone()
         out = torch.empty(t["q"].shape, dtype=torch.float32, device=gu.DEV)
+        ws = torch.zeros(max(plan.workspace_bytes, 256), dtype=torch.uint8, device=gu.DEV)
         if fused:
             sw.swattn_append_verify(desc, t["q"], knd, vnd, sw.SWATTN_BF16, k, v, t["bt"], t["ctx"], 8, w.window,
-                                    w.scale, out, None, 0, stream)
+                                    w.scale, out, ws, plan.workspace_bytes, stream)
         else:
             sw.swattn_append_kv(desc, knd, vnd, sw.SWATTN_BF16, t["bt"], t["ctx"], 8, k, v, stream)
-            sw.swattn_verify(desc, t["q"], k, v, t["bt"], t["ctx"], 8, w.window, w.scale, out, None, 0, stream)
+            sw.swattn_verify(desc, t["q"], k, v, t["bt"], t["ctx"], 8, w.window, w.scale, out, ws,
+                             plan.workspace_bytes, stream)
         torch.cuda.synchronize()
         outs.append(out)
         caches.append((k, v))

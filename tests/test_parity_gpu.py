@@ -581,7 +581,9 @@ def test_column_splits_do_not_change_the_bits():
     t = gu.upload(w)
     outs, splits = {}, {}
     for nb in (48, 24, 1):
-        desc = sw.make_desc(t["q"][:nb], t["k"], t["bt"][:nb], int(w.ctx_len.max()), out_dtype=sw.SWATTN_F32)
+        # one split throughout (a lone problem would otherwise split its keys per tile)
+        desc = sw.make_desc(t["q"][:nb], t["k"], t["bt"][:nb], int(w.ctx_len.max()), out_dtype=sw.SWATTN_F32,
+                            num_splits=1)
         plan = sw.swattn_plan(desc, w.n_q, w.window)
         assert plan.rows_per_chunk == 16 and plan.num_splits == 1, plan.as_dict()
         splits[nb] = plan.grid // (nb * w.Hkv * plan.row_chunks)
