@@ -207,8 +207,17 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// One 16-byte-per-lane global -> LDS copy: lane l's 16 bytes land at lds_dst + 16 l
-// (lds_dst uniform across the wave).  Written as inline assembly on purpose: the
+// The LDS address of an element of a __shared__ array, as a 32-bit offset.  Written for
+// direct array elements only: the destination of a copy is chosen between these offsets,
+// never between generic pointers into different LDS arrays (whose cast back to the LDS
+// address space the compiler lowers with an illegal instruction).
+template <typename T>
+__device__ __forceinline__ uint32_t lds_addr(const T* p) {
+    return (uint32_t)(uintptr_t)LDS_PTR(const void, p);
+}
+
+// One 16-byte-per-lane global -> LDS copy: lane l's 16 bytes land at LDS address
+// lds_dst + 16 l (lds_dst uniform across the wave).  Written as inline assembly on purpose: the
 // compiler then neither tracks it (workgroup barriers do not drain these loads)
 // nor treats it as touching memory (LDS reads of the other stage move freely
 // around it); it stays ordered with barriers and waits, which have side effects.
@@ -217,8 +226,8 @@ __device__ __forceinline__ void wait_vmcnt() {
 // kernels uses M0.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(const void* src, const void* lds_dst) {
-    const uint32_t a = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)LDS_PTR(void, lds_dst));
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_dst) {
+    const uint32_t a = __builtin_amdgcn_readfirstlane(lds_dst);
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(a), "v"(src) : "m0");
 }
 #pragma clang diagnostic pop
@@ -289,9 +298,9 @@ __global__ __launch_bounds__((Geo<D, FP8, KT, RB, CS>::kNT), (Geo<D, FP8, KT, RB
             const unsigned char* src = reinterpret_cast<const unsigned char*>(p.q) +
                                        (((int64_t)b * p.n_q + i) * p.H + h) * G::kRowQ + ((pc ^ G::swz_q(row)) << 4);
             if constexpr (G::kQAlias)
-                dma16(src, &kst[NS - 1][j * 1024]);
+                dma16(src, lds_addr(&kst[NS - 1][j * 1024]));
             else
-                dma16(src, &qst[j * 1024]);
+                dma16(src, lds_addr(&qst[j * 1024]));
         }
     }
 
@@ -410,8 +419,7 @@ __global__ __launch_bounds__((Geo<D, FP8, KT, RB, CS>::kNT), (Geo<D, FP8, KT, RB
             if (j < j0 || j >= j1) continue;
             const int ins = wave * SH + j;       // compile-time j, wave-uniform ins
             const bool is_v = ins >= G::kNiK;
-            unsigned char* dst = (is_v ? vst[t % NS] : kst[t % NS]) + (is_v ? ins - G::kNiK : ins) * 1024;
-            dma16(src[j], dst);
+            dma16(src[j], is_v ? lds_addr(&vst[t % NS][(ins - G::kNiK) * 1024]) : lds_addr(&kst[t % NS][ins * 1024]));
         }
     };
 
@@ -474,7 +482,7 @@ __global__ __launch_bounds__((Geo<D, FP8, KT, RB, CS>::kNT), (Geo<D, FP8, KT, RB
         auto load_one = [=](int j, const unsigned char* from) __attribute__((always_inline)) {
             const int ins = wave * SH + j;       // compile-time j, wave-uniform ins
             const bool is_v = ins >= G::kNiK;
-            dma16(from, (is_v ? vst[tn % NS] : kst[tn % NS]) + (is_v ? ins - G::kNiK : ins) * 1024);
+            dma16(from, is_v ? lds_addr(&vst[tn % NS][(ins - G::kNiK) * 1024]) : lds_addr(&kst[tn % NS][ins * 1024]));
         };
         if (loader) {
             if (prefetch) {
