@@ -32,6 +32,11 @@ CASES = [
     dict(id="many", B=160, n_q=8, ctx_range=(8, 1200), max_blocks=80),
     dict(id="decode", B=6, n_q=1, ctx=[300, 188, 1, 4096, 189, 2000]),
     dict(id="wide", B=2, n_q=64, ctx=[4096, 700]),
+    # 64-row chunks (their 16-row grid would not fit the CUs): 64-key tiles while the grid
+    # fits the CUs (12 x 2 x 4 chunks), 32-key tiles with Q^T in registers beyond them
+    # (130 x 2 chunks)
+    dict(id="tall", B=12, n_q=64, ctx_range=(64, 800), max_blocks=50),
+    dict(id="tall_many", B=130, n_q=16, ctx_range=(16, 600), max_blocks=40),
     # the two-launch form: an E4M3 cache, float32 new rows, the vector-ALU kernel
     dict(id="e4m3_cache", B=3, n_q=8, ctx=[4096, 500, 9], kv="e4m3"),
     dict(id="f32_rows", B=3, n_q=8, ctx=[4096, 500, 9], new="f32"),
@@ -94,6 +99,8 @@ def test_append_verify_equals_append_then_verify(c):
                         num_splits=c.get("S", 0), variant=c.get("variant", 0), merge=c.get("merge", 0))
     plan = sw.swattn_plan(desc, w.n_q, w.window)
     gu.log(f"  plan {plan.as_dict()}")
+    if c["id"] in ("tall", "tall_many"):
+        assert plan.rows_per_chunk == 64 and plan.tile_keys == (64 if c["id"] == "tall" else 32), plan.as_dict()
     stream = torch.cuda.current_stream().cuda_stream
     outs, caches = [], []
     for fused in (True, False):
