@@ -123,6 +123,8 @@ def read_traffic(workload="verify"):
 
 
 def _cpu_info():
+    """CPU model, CPUs this process may run on, and the cgroup CPU quota in CPUs (None
+    when unlimited or unknown)."""
     model = "unknown"
     try:
         with open("/proc/cpuinfo") as f:
@@ -132,7 +134,23 @@ def _cpu_info():
                     break
     except OSError:
         pass
-    return model, len(os.sched_getaffinity(0))
+    quota = None
+    try:                                          # cgroup v2: "<quota> <period>" or "max <period>"
+        with open("/sys/fs/cgroup/cpu.max") as f:
+            q, per = f.read().split()[:2]
+            if q != "max":
+                quota = float(q) / float(per)
+    except (OSError, ValueError):
+        try:                                      # cgroup v1
+            with open("/sys/fs/cgroup/cpu/cpu.cfs_quota_us") as f:
+                q = float(f.read())
+            with open("/sys/fs/cgroup/cpu/cpu.cfs_period_us") as f:
+                per = float(f.read())
+            if q > 0:
+                quota = q / per
+        except (OSError, ValueError):
+            pass
+    return model, len(os.sched_getaffinity(0)), quota
 
 
 _POOL_W = None
@@ -148,6 +166,11 @@ def _pool_init(key):
         pass
     import synth
     _POOL_W = synth.named_workload(key)
+    try:                                          # numpy is loaded now: limit its BLAS too
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(limits=1)
+    except Exception:
+        pass
 
 
 def _pool_slice(b0, b1):
@@ -181,7 +204,7 @@ def cpu_baseline(key, budget_s):
     import synth
     from threadpoolctl import threadpool_limits
     w = synth.named_workload(key)
-    model, allowed = _cpu_info()
+    model, allowed, quota = _cpu_info()
 
     def call():
         oracle.attend(w.q, w.k_cache, w.v_cache, w.block_table, w.ctx_len, w.n_q, w.window, w.scale,
@@ -193,12 +216,27 @@ def cpu_baseline(key, budget_s):
         c0 = time.process_time()
         tall = _time_reps(call, budget_s / 3, 5)
         eff = (time.process_time() - c0) / max(sum(tall), 1e-9)
-    workers = max(1, min(allowed, 16))
+    # one process per CPU the process may use: allowed CPUs, capped by the cgroup quota
+    usable = allowed if quota is None else max(1, min(allowed, int(quota)))
+    workers = max(1, min(usable, 16))
     per_task = max(1, -(-w.B // (4 * workers)))
     tasks = [(b, min(w.B, b + per_task)) for b in range(0, w.B, per_task)]
-    with mp.get_context("spawn").Pool(workers, initializer=_pool_init, initargs=(key,)) as pool:
-        pool.starmap(_pool_slice, tasks)          # every worker built its workload
-        tpool = _time_reps(lambda: pool.starmap(_pool_slice, tasks), budget_s / 3, 20)
+    # The workers are fresh interpreters: their BLAS reads its thread count from the
+    # environment when numpy loads, so one thread each is set there (with 16 BLAS threads
+    # per worker the pool oversubscribes the CPUs).
+    thread_vars = ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS", "BLIS_NUM_THREADS")
+    saved = {k: os.environ.get(k) for k in thread_vars}
+    os.environ.update({k: "1" for k in thread_vars})
+    try:
+        with mp.get_context("spawn").Pool(workers, initializer=_pool_init, initargs=(key,)) as pool:
+            pool.starmap(_pool_slice, tasks)          # every worker built its workload
+            tpool = _time_reps(lambda: pool.starmap(_pool_slice, tasks), budget_s / 3, 20)
+    finally:
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
     us = lambda ts: round(statistics.median(ts) * 1e6, 1)
     return {"value": us(tpool), "unit": "us/call", "cores": workers, "kind": "oracle",
             "sample": f"whole workload per call ({w.B} sequences); process pool: {workers} processes x 1 BLAS "
@@ -206,7 +244,8 @@ def cpu_baseline(key, budget_s):
             "single_thread": {"value": us(t1), "unit": "us/call", "reps": len(t1)},
             "blas_all_threads": {"value": us(tall), "unit": "us/call", "blas_threads": allowed,
                                  "effective_cores": round(eff, 2), "reps": len(tall)},
-            "cpu_model": model, "host_cpus_allowed": allowed}
+            "cpu_model": model, "host_cpus_allowed": allowed, "cgroup_cpu_quota": quota,
+            "pool_speedup_vs_single_thread": round(us(t1) / max(us(tpool), 1e-9), 2)}
 
 
 class ColdFlush:
@@ -346,6 +385,8 @@ def main():
                          "swattn_window_gather, the workload's data movement without arithmetic")
     ap.add_argument("--vocab", type=int, default=262144, help="accept op: logits per position")
     ap.add_argument("--accept-batch", type=int, default=1, help="accept op: sequences per call")
+    ap.add_argument("--gather-parts", type=int, default=1,
+                    help="gather_ceiling op: workgroups per (problem, KV head), each a slice of its rows")
     ap.add_argument("--calibrate-copy", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -394,7 +435,8 @@ def main():
                 "value": r["value"], "unit": "us/call", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
                 "ms_per_step": round(r["value"] / 1e3, 6), "higher_is_better": False, "scaling": "weak",
                 "vs_baseline": None, "dtype": r["dtype"], "data": "synthetic", "config": r["config"],
-                "roofline": r["roofline"], "timing": r["timing"], "cpu_baseline": None}
+                "roofline": r["roofline"], "timing": r["timing"], "cpu_baseline": None,
+                "gather_parts": args.gather_parts}
         print(json.dumps(line), flush=True)
         return
 
@@ -421,19 +463,27 @@ def main():
     }
     ok = res["parity_spot_check"]["ok"]
     if args.workload == WORKLOAD and not args.no_extra:
+        # the same bytes without arithmetic, spread over four workgroups per (layer, KV head)
+        # (the fastest spread measured; the kernel's four workgroups re-read their unit's K)
+        c = measure_attention(args.workload, args, torch, np, sw, synth, dev, gather=True, gather_parts=4)
+        line["gather_ceiling"] = {"value": c["value"], "unit": "us/call", "frac": c["roofline"]["frac"],
+                                  "parts": 4,
+                                  "what": "swattn_window_gather on the same inputs, four workgroups per "
+                                          "(layer, KV head): the algorithmic bytes and paged loads, no arithmetic"}
         # the batched configuration carries the bandwidth target: measured in the same run
         line["batched"] = {}
         for key in ("batched_fp8", "batched_bf16"):
             r = measure_attention(key, args, torch, np, sw, synth, dev)
-            c = measure_attention(key, args, torch, np, sw, synth, dev, gather=True)
+            c = measure_attention(key, args, torch, np, sw, synth, dev, gather=True, gather_parts=1)
             line["batched"][key] = {"value": r["value"], "unit": "us/call", "dtype": r["dtype"],
                                     "workload": r["config"]["workload"], "roofline": r["roofline"],
                                     "cold_eager_us_median": r["timing"]["cold_eager_us_median"],
                                     "plan": r["plan"], "parity_spot_check": r["parity_spot_check"],
                                     "gather_ceiling": {"value": c["value"], "unit": "us/call",
-                                                       "frac": c["roofline"]["frac"],
+                                                       "frac": c["roofline"]["frac"], "parts": 1,
                                                        "what": "swattn_window_gather on the same inputs: the same "
-                                                               "bytes and paged loads, no arithmetic"}}
+                                                               "bytes and paged loads, no arithmetic (one "
+                                                               "workgroup per unit; more measured slower)"}}
             ok = ok and r["parity_spot_check"]["ok"]
     print(json.dumps(line), flush=True)
     if not ok:
@@ -441,7 +491,7 @@ def main():
         sys.exit(1)
 
 
-def measure_attention(key, args, torch, np, sw, synth, dev, gather=False):
+def measure_attention(key, args, torch, np, sw, synth, dev, gather=False, gather_parts=None):
     """Cold per-call time of swattn_verify (or swattn_prefill for chunks above 64
     positions) on a named workload, its roofline fraction and an oracle spot check;
     with gather=True, of swattn_window_gather on the same inputs (no spot check)."""
@@ -472,7 +522,8 @@ def measure_attention(key, args, torch, np, sw, synth, dev, gather=False):
 
     def launch(cs):
         if gather:
-            sw.swattn_window_gather(desc, q, k, v, bt, ctx, w.n_q, w.window, out, cs)
+            sw.swattn_window_gather(desc, q, k, v, bt, ctx, w.n_q, w.window,
+                                    args.gather_parts if gather_parts is None else gather_parts, out, cs)
         else:
             call_lib(desc, q, k, v, bt, ctx, w.n_q, w.window, w.scale, out, ws, plan.workspace_bytes, cs)
 

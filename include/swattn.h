@@ -355,8 +355,10 @@ swattn_status_t swattn_verify_noalloc(const swattn_desc_t* desc,
  * loads as the attention kernel, all requested at once), reads the problem's Q rows,
  * and writes zeros over its rows of `out`: exactly the bytes counted as the verify
  * call's algorithmic traffic, so its time is the data-movement floor of that paged
- * layout and launch shape.  Arguments and host-side checks as swattn_verify (no
- * workspace); `out` receives zeros.  A window of more than 1024 positions is read over
+ * layout and launch shape.  `parts` (1..16, else SWATTN_ERR_ARG) workgroups share each
+ * (problem, KV head), each taking a contiguous slice of its window rows, Q rows and
+ * output rows.  Other arguments and host-side checks as swattn_verify (no workspace);
+ * `out` receives zeros.  A window of more than 1024 positions is read over
  * its first 1024, and at most 512 query rows per KV head.  Source of the window rule:
  * "The Fast Gemma Challenge: our verified-SOTA recipe, in full", manifest
  * SLIDING_WINDOW, SPECULATIVE_CONFIG; "What each piece does, and why" (decode is bound
@@ -365,7 +367,7 @@ swattn_status_t swattn_verify_noalloc(const swattn_desc_t* desc,
 swattn_status_t swattn_window_gather(const swattn_desc_t* desc,
                                      const void* q, const void* k_cache, const void* v_cache,
                                      const int32_t* block_table, const int32_t* ctx_len,
-                                     int32_t n_q, int32_t window, void* out, void* stream);
+                                     int32_t n_q, int32_t window, int32_t parts, void* out, void* stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char* swattn_status_str(swattn_status_t status);

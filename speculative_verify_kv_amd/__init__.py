@@ -106,7 +106,7 @@ def lib():
         L.swattn_verify_noalloc.restype = ctypes.c_int
         L.swattn_window_gather.argtypes = [P(swattn_desc_t), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
-                                           ctypes.c_void_p, ctypes.c_void_p]
+                                           ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
         L.swattn_window_gather.restype = ctypes.c_int
         L.swattn_prefill_plan.argtypes = L.swattn_plan.argtypes
         L.swattn_prefill_plan.restype = ctypes.c_int
@@ -207,10 +207,10 @@ def swattn_verify_noalloc(desc, q, k_cache, v_cache, block_table, ctx_len, n_q, 
     return st
 
 
-def swattn_window_gather(desc, q, k_cache, v_cache, block_table, ctx_len, n_q, window, out, stream=None,
+def swattn_window_gather(desc, q, k_cache, v_cache, block_table, ctx_len, n_q, window, parts, out, stream=None,
                          check=True):
     st = lib().swattn_window_gather(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
-                                    _ptr(ctx_len), int(n_q), int(window), _ptr(out), _ptr(stream))
+                                    _ptr(ctx_len), int(n_q), int(window), int(parts), _ptr(out), _ptr(stream))
     if check and st != 0:
         raise SwattnError(st, "swattn_window_gather")
     return st

@@ -1,14 +1,16 @@
 // swattn_window_gather: the data movement of a verify call without its arithmetic, as a
 // measurement of the floor that the paged layout and the launch shape set.
 //
-// One workgroup per (problem b, KV head g) moves exactly the bytes the verify call's
-// algorithmic count covers: the K and V rows of the union of its queries' windows
-// (positions ctx_len[b] - n_q - window + 1 .. ctx_len[b] - 1, clipped at 0), read
-// through the block table with the same 16-byte global-to-LDS loads as the partition
-// kernel, all requested at once; its Q rows, the same way; and an output-sized write
-// of zeros.  Nothing is computed.  The loaded bytes land in one LDS buffer that is
-// overwritten freely; every load is waited for before the workgroup ends.  A window of
-// more than 1024 rows is measured over its first 1024 (and at most 512 Q rows).
+// `parts` workgroups per (problem b, KV head g) move exactly the bytes the verify
+// call's algorithmic count covers: the K and V rows of the union of its queries'
+// windows (positions ctx_len[b] - n_q - window + 1 .. ctx_len[b] - 1, clipped at 0),
+// read through the block table with the same 16-byte global-to-LDS loads as the
+// partition kernel, all requested at once; its Q rows, the same way; and an
+// output-sized write of zeros.  Workgroup p of a unit takes the p-th contiguous slice
+// of each (window rows, Q rows, output rows).  Nothing is computed.  The loaded bytes
+// land in one LDS buffer that is overwritten freely; every load is waited for before
+// the workgroup ends.  A window of more than 1024 rows is measured over its first 1024
+// (and at most 512 Q rows).
 //
 // The window rule follows "The Fast Gemma Challenge: our verified-SOTA recipe, in
 // full" (manifest SLIDING_WINDOW, SPECULATIVE_CONFIG; "What each piece does, and
@@ -53,6 +55,7 @@ struct GatherParams {
     int32_t Hkv, G, H, D, bs, max_blocks, num_blocks, max_ctx, n_q, window;
     int32_t kv_elt, q_elt, out_elt;
     int32_t lg_cpr, lg_qcpr;              // log2 of the 16-byte chunks of a cache row / a Q row
+    int32_t parts;                        // workgroups per (problem, KV head)
 };
 
 __global__ __launch_bounds__(kGatherThreads) void window_gather_kernel(GatherParams p) {
@@ -62,16 +65,20 @@ __global__ __launch_bounds__(kGatherThreads) void window_gather_kernel(GatherPar
     __shared__ int64_t rowoff[kGatherMaxRows + kGatherMaxQRows];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int b = blockIdx.x / p.Hkv, g = blockIdx.x % p.Hkv;
+    const int unit = blockIdx.x / p.parts, part = blockIdx.x % p.parts;
+    const int b = unit / p.Hkv, g = unit % p.Hkv;
     const int ctx = p.ctx_len[b];
     const bool ok = ctx >= p.n_q && ctx <= p.max_blocks * p.bs && ctx <= p.max_ctx;
     const int u_hi = ok ? ctx : 0;                                    // one past the last key
     const int u_lo = ok ? max(0, ctx - p.n_q - p.window + 1) : 0;
-    const int nrows = min(u_hi - u_lo, kGatherMaxRows);
-    const int q_rows = min(p.n_q * p.G, kGatherMaxQRows);
+    const int n_all = min(u_hi - u_lo, kGatherMaxRows);
+    const int q_all = min(p.n_q * p.G, kGatherMaxQRows);
+    // this workgroup's slices: window rows [w0, w0 + nrows), Q and output rows [r0, r0 + q_rows)
+    const int w0 = n_all * part / p.parts, nrows = n_all * (part + 1) / p.parts - w0;
+    const int r0 = q_all * part / p.parts, q_rows = q_all * (part + 1) / p.parts - r0;
     const int row_b = p.D * p.kv_elt;                                 // bytes per cache row
     for (int t = tid; t < nrows; t += kGatherThreads) {
-        const int j = u_lo + t;
+        const int j = u_lo + w0 + t;
         const int blk = j / p.bs;
         const int phys = p.block_table[(int64_t)b * p.max_blocks + blk];
         // a row in an out-of-range block is read from row 0 instead (same byte count)
@@ -79,7 +86,7 @@ __global__ __launch_bounds__(kGatherThreads) void window_gather_kernel(GatherPar
                                                      : 0;
     }
     for (int r = tid; r < q_rows; r += kGatherThreads) {
-        const int i = r / p.G, h = g * p.G + (r - i * p.G);
+        const int i = (r0 + r) / p.G, h = g * p.G + (r0 + r - i * p.G);
         rowoff[kGatherMaxRows + r] = (((int64_t)b * p.n_q + i) * p.H + h) * (p.D * p.q_elt);
     }
     __syncthreads();
@@ -129,13 +136,14 @@ __global__ __launch_bounds__(kGatherThreads) void window_gather_kernel(GatherPar
 
 extern "C" swattn_status_t swattn_window_gather(const swattn_desc_t* d, const void* q, const void* k_cache,
                                                 const void* v_cache, const int32_t* block_table,
-                                                const int32_t* ctx_len, int32_t n_q, int32_t window, void* out,
-                                                void* stream) {
+                                                const int32_t* ctx_len, int32_t n_q, int32_t window, int32_t parts,
+                                                void* out, void* stream) {
     using namespace swattn;
     swattn_plan_t plan;
     swattn_status_t st = make_plan(d, n_q, window, SWATTN_MAX_NQ, &plan);   // the same argument checks
     if (st != SWATTN_OK) return st;
     if (!q || !k_cache || !v_cache || !block_table || !ctx_len || !out) return SWATTN_ERR_NULL;
+    if (parts < 1 || parts > 16) return SWATTN_ERR_ARG;
     const auto al = [](const void* x, uintptr_t a) { return (reinterpret_cast<uintptr_t>(x) & (a - 1)) == 0; };
     if (!al(q, 16) || !al(k_cache, 16) || !al(v_cache, 16) || !al(out, 16) || !al(block_table, 4) || !al(ctx_len, 4))
         return SWATTN_ERR_ALIGN;
@@ -163,7 +171,8 @@ extern "C" swattn_status_t swattn_window_gather(const swattn_desc_t* d, const vo
     while ((16 << p.lg_cpr) < p.D * p.kv_elt) ++p.lg_cpr;      // rows are 64 * 2^k bytes
     p.lg_qcpr = 0;
     while ((16 << p.lg_qcpr) < p.D * p.q_elt) ++p.lg_qcpr;
-    const int64_t grid = (int64_t)d->batch * d->num_kv_heads;
+    p.parts = parts;
+    const int64_t grid = (int64_t)d->batch * d->num_kv_heads * parts;
     if (grid > INT32_MAX) return SWATTN_ERR_SHAPE;
     hipLaunchKernelGGL(window_gather_kernel, dim3((unsigned)grid), dim3(kGatherThreads), 0,
                        reinterpret_cast<hipStream_t>(stream), p);

@@ -690,13 +690,20 @@ def test_e4m3_decode_column_quarters_fused_merge(B):
 # ---------------------------------------------------------------------------
 # the measurement aid: the verify call's data movement without arithmetic
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("key", ["batched_fp8", "verify", "tiny_decode"])
-def test_window_gather_moves_the_data_and_writes_zeros(key):
+@pytest.mark.parametrize("key,parts", [("batched_fp8", 1), ("batched_fp8", 3), ("verify", 1), ("verify", 4),
+                                       ("tiny_decode", 1), ("tiny_decode", 2)])
+def test_window_gather_moves_the_data_and_writes_zeros(key, parts):
+    # every output row is written (zeros) whatever the number of workgroups per unit,
+    # including slices that split rows unevenly; out-of-range part counts are refused
     w, _ = gu.named(key)
     t = gu.upload(w)
     out = torch.full(t["q"].shape, 7.0, dtype=torch.float32 if w.q_dtype == "f32" else torch.bfloat16, device=gu.DEV)
     desc = sw.make_desc(t["q"], t["k"], t["bt"], int(w.ctx_len.max()), k_scale=t["ks"], v_scale=t["vs"])
-    sw.swattn_window_gather(desc, t["q"], t["k"], t["v"], t["bt"], t["ctx"], w.n_q, w.window, out,
-                            torch.cuda.current_stream().cuda_stream)
+    stream = torch.cuda.current_stream().cuda_stream
+    sw.swattn_window_gather(desc, t["q"], t["k"], t["v"], t["bt"], t["ctx"], w.n_q, w.window, parts, out, stream)
     torch.cuda.synchronize()
     assert int(out.count_nonzero()) == 0
+    for bad in (0, 17):
+        st = sw.swattn_window_gather(desc, t["q"], t["k"], t["v"], t["bt"], t["ctx"], w.n_q, w.window, bad, out,
+                                     stream, check=False)
+        assert sw.STATUS[st] == "SWATTN_ERR_ARG"
