@@ -1,19 +1,21 @@
 // Split-KV partition kernel on gfx950 matrix cores (bf16 MFMA 16x16x32).
 //
-// One workgroup owns one (problem b, KV head g, row chunk, KV split s).  A KV
-// head's query rows are its n_q queries times the H/Hkv heads that share it
-// (row r = i * G + head-in-group), so a verify step with n_q = 8 and GQA 4 is
+// One workgroup owns one (problem b, KV head g, row chunk, column split, KV split
+// s).  A KV head's query rows are its n_q queries times the H/Hkv heads that share
+// it (row r = i * G + head-in-group), so a verify step with n_q = 8 and GQA 4 is
 // one dense 32-row tile.  Launches that leave most CUs idle take 16-row chunks,
-// each run by two workgroups that split the output columns (both load all K rows
-// and compute the same scores; each loads its half of every V row).  The split's
-// keys are walked in tiles of 64 (or 32) through an LDS ring filled by direct
-// global-to-LDS loads.
+// each run by two or four workgroups that split the output columns (all load every
+// K row and compute the same scores; each loads its part of every V row); launches
+// with many rows per KV head take 64-row chunks, so that each K/V tile serves more
+// rows.  The split's keys are walked in tiles of 64 (or 32) through an LDS ring
+// filled by direct global-to-LDS loads.
 //
 // With 64-key tiles, compute wave w owns 16 query rows (a row block), one 32-key
 // half of every tile's keys, with an online softmax of its own, and a set of the
-// workgroup's output columns: all of them when two workgroups fit in a CU's LDS,
-// half of them otherwise (so that a SIMD still runs two waves).  With 32-key tiles
-// every wave takes all keys of its row block and the waves split the columns.
+// workgroup's output columns: all of them when two workgroups fit in a CU's LDS or
+// the chunk has 64 rows, half of them otherwise (so that a SIMD still runs two
+// waves).  With 32-key tiles every wave takes all keys of its row block; in 32-row
+// chunks the waves split the columns, in 64-row chunks each wave has all of them.
 // 16-row workgroups add as many loader waves, which only load and pass barriers.
 // Per tile:
 //   S^T = K . Q^T        matrix cores; K rows from LDS, Q^T in registers for the
@@ -98,10 +100,10 @@ struct Geo {
     // (A CU's load rate, about 30-45 GB/s, bounds these chains: rings that request
     // every tile of a chunk up front measured slower, since tile 0 then lands later.)
     static constexpr int kNS = 2 * (4 * kStageB + 14 * 1024) <= 160 * 1024 ? 4 : 2;
-    // Workgroups per CU that the LDS allows.  Where only one fits, the workgroup splits
-    // the output columns across two wave sets (8 waves) so that every SIMD still holds
-    // two waves; otherwise it has 4 waves.  Either way a SIMD runs two waves, so each
-    // may hold 256 registers.
+    // Workgroups per CU that the LDS allows.  Where only one fits, the workgroup has 8
+    // waves (32-row chunks split the output columns across two wave sets, 64-row chunks
+    // have four row blocks) so that every SIMD still holds two waves; otherwise it has
+    // 4 waves.  Either way a SIMD runs two waves, so each may hold 256 registers.
     static constexpr int kBlocks = 2 * (kNS * kStageB + 14 * 1024) <= 160 * 1024 ? 2 : 1;
     // Where two workgroups share a CU, and in 64-row chunks (whose 32 KiB of Q rows would
     // not fit beside the ring), the prologue leaves the last ring stage free (its tile goes
