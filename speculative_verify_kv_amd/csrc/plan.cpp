@@ -141,7 +141,9 @@ swattn_status_t make_plan(const swattn_desc_t* d, int32_t n_q, int32_t window, i
         // workgroups by output columns (each reading all K rows and its part of every V
         // row).  The outputs stay disjoint, so nothing merges (one verify step of 24
         // layers: 32-row chunks 15.0 us, 16-row chunks 12.1 us, split by columns too
-        // 11.2 us; plain decode 12.1 -> 10.4 us).
+        // 11.2 us; plain decode 12.1 -> 10.4 us).  Otherwise bfloat16 launches with 64
+        // rows or more per KV head take 64-row chunks, whose K/V tiles serve twice the
+        // rows (prefill of 512 positions 99.6 -> 68.6 us, wide verify 20.3 -> 18.3 us).
         const int64_t g16 = (int64_t)d->batch * d->num_kv_heads * ((R + 15) / 16) * S;
         if (kMfmaHalfRows && d->head_dim == 256 && g16 <= kComputeUnits) {
             rows_per_chunk = kMfmaRows / 2;
