@@ -16,6 +16,14 @@
 // Kernel 1: one workgroup per (row, chunk of kAcceptChunk logits) reduces its chunk
 // to one key in the workspace.  Kernel 2: one wave per sequence reduces the chunk
 // keys of its n_q rows, writes the target ids, and scans the drafts.
+//
+// Inside a thread, whose logits come in increasing index order, the running maximum
+// is kept as a float with its index, replaced only by a strictly larger value: the
+// first index of the largest value wins and -0 equals +0, as the key order says, at
+// three instructions per logit.  NaN never compares larger, so every logit is also
+// added into a probe sum; a thread whose probe turns out NaN (a NaN logit, or inf and
+// -inf together) scans its logits again for the first NaN.  The key is built once per
+// thread from the result.
 
 #include <hip/hip_runtime.h>
 
@@ -44,6 +52,29 @@ __device__ __forceinline__ uint64_t wave_max(uint64_t k) {
     return k;
 }
 
+// Running (maximum, index) of one thread, and the NaN probe.  The index starts at
+// the thread's first logit, which is the answer when every logit is -inf.
+struct ArgmaxRun {
+    float best = -INFINITY;
+    uint32_t idx;
+    float probe = 0.0f;
+    __device__ __forceinline__ explicit ArgmaxRun(uint32_t first) : idx(first) {}
+    __device__ __forceinline__ void add(float v, uint32_t i) {
+        const bool gt = v > best;
+        best = gt ? v : best;
+        idx = gt ? i : idx;
+        probe += v;
+    }
+};
+
+template <bool BF16>
+__device__ __forceinline__ float logit_at(const void* row, int64_t v) {
+    if constexpr (BF16)
+        return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(row)[v] << 16);
+    else
+        return reinterpret_cast<const float*>(row)[v];
+}
+
 template <bool BF16>
 __global__ __launch_bounds__(kBlockThreads) void argmax_chunks_kernel(AcceptParams p) {
     const int nchunk = p.nchunk;
@@ -56,7 +87,9 @@ __global__ __launch_bounds__(kBlockThreads) void argmax_chunks_kernel(AcceptPara
         const uint16_t* L = reinterpret_cast<const uint16_t*>(p.logits) + row * p.vocab;
         if (p.vec_ok) {                                           // 8 logits per 16-byte load, 4 loads in flight
             constexpr int U = 4;
-            for (int64_t v = v0 + (int64_t)threadIdx.x * 8; v < v1; v += (int64_t)kBlockThreads * 8 * U) {
+            const int64_t first = v0 + (int64_t)threadIdx.x * 8;
+            ArgmaxRun run((uint32_t)first);
+            for (int64_t v = first; v < v1; v += (int64_t)kBlockThreads * 8 * U) {
                 uint4 w[U];
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
@@ -70,13 +103,26 @@ __global__ __launch_bounds__(kBlockThreads) void argmax_chunks_kernel(AcceptPara
                     const uint32_t ww[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
 #pragma unroll
                     for (int k = 0; k < 4; ++k) {
-                        const uint64_t a = argmax_key(__uint_as_float(ww[k] << 16), (uint32_t)(vu + 2 * k));
-                        const uint64_t b = argmax_key(__uint_as_float(ww[k] & 0xFFFF0000u), (uint32_t)(vu + 2 * k + 1));
-                        best = a > best ? a : best;
-                        best = b > best ? b : best;
+                        run.add(__uint_as_float(ww[k] << 16), (uint32_t)(vu + 2 * k));
+                        run.add(__uint_as_float(ww[k] & 0xFFFF0000u), (uint32_t)(vu + 2 * k + 1));
                     }
                 }
             }
+            if (run.probe != run.probe) {                         // a NaN among this thread's logits?
+                for (int64_t v = first; v < v1; v += (int64_t)kBlockThreads * 8) {
+                    int k = 0;
+                    for (; k < 8 && v + k < v1; ++k) {
+                        const float x = logit_at<true>(L, v + k);
+                        if (x != x) break;
+                    }
+                    if (k < 8 && v + k < v1) {
+                        run.best = __builtin_nanf("");
+                        run.idx = (uint32_t)(v + k);
+                        break;
+                    }
+                }
+            }
+            if (first < v1) best = argmax_key(run.best, run.idx);
         } else {
             for (int64_t v = v0 + threadIdx.x; v < v1; v += kBlockThreads) {
                 const uint64_t a = argmax_key(__uint_as_float((uint32_t)L[v] << 16), (uint32_t)v);
@@ -87,7 +133,9 @@ __global__ __launch_bounds__(kBlockThreads) void argmax_chunks_kernel(AcceptPara
         const float* L = reinterpret_cast<const float*>(p.logits) + row * p.vocab;
         if (p.vec_ok) {                                           // 4 logits per 16-byte load, 4 loads in flight
             constexpr int U = 4;
-            for (int64_t v = v0 + (int64_t)threadIdx.x * 4; v < v1; v += (int64_t)kBlockThreads * 4 * U) {
+            const int64_t first = v0 + (int64_t)threadIdx.x * 4;
+            ArgmaxRun run((uint32_t)first);
+            for (int64_t v = first; v < v1; v += (int64_t)kBlockThreads * 4 * U) {
                 float4 f[U];
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
@@ -100,12 +148,24 @@ __global__ __launch_bounds__(kBlockThreads) void argmax_chunks_kernel(AcceptPara
                     if (vu >= v1) break;
                     const float ff[4] = {f[u].x, f[u].y, f[u].z, f[u].w};
 #pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        const uint64_t a = argmax_key(ff[k], (uint32_t)(vu + k));
-                        best = a > best ? a : best;
+                    for (int k = 0; k < 4; ++k) run.add(ff[k], (uint32_t)(vu + k));
+                }
+            }
+            if (run.probe != run.probe) {                         // a NaN among this thread's logits?
+                for (int64_t v = first; v < v1; v += (int64_t)kBlockThreads * 4) {
+                    int k = 0;
+                    for (; k < 4 && v + k < v1; ++k) {
+                        const float x = logit_at<false>(L, v + k);
+                        if (x != x) break;
+                    }
+                    if (k < 4 && v + k < v1) {
+                        run.best = __builtin_nanf("");
+                        run.idx = (uint32_t)(v + k);
+                        break;
                     }
                 }
             }
+            if (first < v1) best = argmax_key(run.best, run.idx);
         } else {
             for (int64_t v = v0 + threadIdx.x; v < v1; v += kBlockThreads) {
                 const uint64_t a = argmax_key(L[v], (uint32_t)v);
