@@ -44,6 +44,22 @@ def make_case(B, n_q, vocab, seed, bf16, specials=False):
             x[0, 2, :] = -np.inf              # all equal: index 0
         if n_q > 3:
             x[0, 3, 7] = np.inf
+        if n_q > 7:
+            # inf and -inf without a NaN (their sum is NaN: the scan's NaN probe fires and
+            # finds none): the first +inf wins
+            x[0, 4, 2] = -np.inf
+            x[0, 4, 4] = np.inf
+            x[0, 4, vocab - 1] = np.inf
+            # a single NaN in an otherwise -inf row, at the last index
+            x[0, 5, :] = -np.inf
+            x[0, 5, vocab - 1] = np.nan
+            # the largest value a positive denormal, the larger of two coming later
+            x[0, 6, :] = -1.0
+            x[0, 6, 1] = 1e-40
+            x[0, 6, min(vocab - 1, 5000)] = 2e-40
+            # an early +inf, then a NaN far later (another thread, for long rows): NaN wins
+            x[0, 7, 0] = np.inf
+            x[0, 7, min(vocab - 1, 4099)] = np.nan
     if bf16:
         bits = oracle.f32_to_bf16_rne(x)
         vals = (bits.astype(np.uint32) << 16).view(np.float32)
