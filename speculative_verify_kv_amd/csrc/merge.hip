@@ -5,7 +5,7 @@
 // SPLITKV_VERIFY, "Published files").
 //
 // D/4 lanes per row, each owning 4 consecutive dims (16-byte loads of every
-// partial), 1024/D rows per 256-thread workgroup.
+// partial), 4 kMergeThreads / D rows per workgroup.
 
 #include <hip/hip_runtime.h>
 
@@ -17,9 +17,9 @@ namespace swattn {
 namespace {
 
 template <int D, bool OUT_F32>
-__global__ __launch_bounds__(kBlockThreads) void merge_kernel(MergeParams p) {
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeParams p) {
     constexpr int TPR = D / 4;
-    constexpr int RPW = kBlockThreads / TPR;
+    constexpr int RPW = kMergeThreads / TPR;
     const int64_t rows_total = (int64_t)p.B * p.Hkv * p.R;
     const int64_t row = (int64_t)blockIdx.x * RPW + threadIdx.x / TPR;
     if (row >= rows_total) return;
@@ -40,9 +40,9 @@ __global__ __launch_bounds__(kBlockThreads) void merge_kernel(MergeParams p) {
 template <int D>
 int launch_d(const MergeParams& p, int grid, hipStream_t st) {
     if (p.out_dtype == SWATTN_F32)
-        hipLaunchKernelGGL((merge_kernel<D, true>), dim3(grid), dim3(kBlockThreads), 0, st, p);
+        hipLaunchKernelGGL((merge_kernel<D, true>), dim3(grid), dim3(kMergeThreads), 0, st, p);
     else
-        hipLaunchKernelGGL((merge_kernel<D, false>), dim3(grid), dim3(kBlockThreads), 0, st, p);
+        hipLaunchKernelGGL((merge_kernel<D, false>), dim3(grid), dim3(kMergeThreads), 0, st, p);
     return (int)hipGetLastError();
 }
 

@@ -187,7 +187,7 @@ swattn_status_t make_plan(const swattn_desc_t* d, int32_t n_q, int32_t window, i
     if (variant == SWATTN_VARIANT_MFMA && (row_chunks * col_splits > 65535 || S > 65535)) return SWATTN_ERR_SHAPE;
 
     const int64_t rows_total = (int64_t)d->batch * d->num_kv_heads * R;
-    const int64_t merge_rows_per_wg = (kBlockThreads * 4) / D;   // D/4 threads per row
+    const int64_t merge_rows_per_wg = (kMergeThreads * 4) / D;   // D/4 threads per row
     int64_t merge_grid = 0;
     int32_t fused = 0;
     size_t ws = 0;

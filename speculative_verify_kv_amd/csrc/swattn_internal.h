@@ -10,7 +10,8 @@ namespace swattn {
 
 // Launch geometry shared by the planner and the kernels.
 constexpr int kWaveSize = 64;
-constexpr int kBlockThreads = 256;           // 4 waves: VALU partition and merge kernels
+constexpr int kBlockThreads = 256;           // 4 waves: VALU partition, argmax, append and fill kernels
+constexpr int kMergeThreads = 256;           // merge kernel workgroup (D/4 threads per row)
 constexpr int kMfmaRows = 32;                // query rows per matrix-core workgroup (two 16-row tiles)
 constexpr int kMfmaMaxKeys = 512;            // keys per matrix-core workgroup (cache-row table in LDS)
 constexpr int kComputeUnits = 256;           // MI355X
