@@ -32,7 +32,9 @@ bool dtype_in(int v, std::initializer_list<int> ok) {
     return false;
 }
 
-int64_t clamp64(int64_t v, int64_t lo, int64_t hi) { return v < lo ? lo : (v > hi ? hi : v); }
+// v limited to [lo, hi]; where the bounds cross, the lower one wins (split counts: the
+// least that keeps every split within its workgroup's key table beats any preference)
+int64_t clamp64(int64_t v, int64_t lo, int64_t hi) { return std::max(lo, std::min(v, hi)); }
 
 }  // namespace
 
@@ -179,6 +181,14 @@ swattn_status_t make_plan(const swattn_desc_t* d, int32_t n_q, int32_t window, i
             S = clamp64(d->num_splits, s_min, U);
         else
             S = clamp64((kFillTarget + units - 1) / units, s_min, s_cap);
+    }
+    // Every split of every row chunk within its workgroup's key table (the rules above
+    // guarantee it; a plan that broke it would overrun the table in LDS)
+    {
+        const int64_t qpc_f = std::min<int64_t>(n_q, (rows_per_chunk - 1) / G + 2);
+        const int64_t U_f = std::min<int64_t>(d->max_ctx_len, (int64_t)window + qpc_f - 1);
+        const int64_t table = variant == SWATTN_VARIANT_MFMA ? kMfmaMaxKeys : kValuMaxKeys;
+        if ((U_f + S - 1) / S > table) return SWATTN_ERR_SHAPE;
     }
     const int64_t row_chunks = (R + rows_per_chunk - 1) / rows_per_chunk;
     const int64_t grid = (int64_t)d->batch * d->num_kv_heads * row_chunks * col_splits * S;

@@ -299,3 +299,52 @@ def test_verify_host_checks_return_before_launch():
     assert call(n_q=65) == "SWATTN_ERR_NQ"
     assert call(window=0) == "SWATTN_ERR_WINDOW"
     assert lib.swattn_check_inputs(ctypes.byref(d), None, 5 * A, 8, 188, None) == -1
+
+
+def _longest_split(plan, n_q, G, window, ctx):
+    """Most keys one workgroup scans under `plan` for a sequence of length ctx: the
+    union of the windows of a row chunk's queries, in plan.num_splits near-equal parts
+    (brute force over the chunks)."""
+    R = n_q * G
+    pos0 = ctx - n_q
+    worst = 0
+    for rc in range(plan.row_chunks):
+        qs = [r // G for r in range(rc * plan.rows_per_chunk, min(R, (rc + 1) * plan.rows_per_chunk))]
+        lo = max(0, pos0 + min(qs) - window + 1)
+        hi = pos0 + max(qs) + 1
+        worst = max(worst, -(-(hi - lo) // plan.num_splits))
+    return worst
+
+
+@pytest.mark.parametrize("kv", ["bf16", "e4m3", "f32"])
+def test_every_split_fits_the_key_table(kv):
+    # A workgroup keeps the source row of every key it scans in an LDS table of 512
+    # entries (matrix-core kernel) or 256 (vector-ALU kernel); the plan must split long
+    # ranges so that no workgroup scans more, whatever the launch size (single-sequence
+    # full attention past 4096 keys included).
+    kvd = {"bf16": sw.SWATTN_BF16, "e4m3": sw.SWATTN_FP8_E4M3, "f32": sw.SWATTN_F32}[kv]
+    extra = dict(k_scale=16, v_scale=32) if kv == "e4m3" else {}
+    checked = 0
+    for D in (64, 128, 256):
+        for H, Hkv in ((8, 2), (8, 8), (8, 1)):
+            for batch in (1, 2, 8, 24, 200):
+                for max_ctx in (300, 4096, 8192, 40000):
+                    for n_q, window in ((1, 188), (8, 188), (1, 10 ** 6), (8, 10 ** 6), (64, 5000), (3, 2000)):
+                        if n_q > max_ctx:
+                            continue
+                        d = desc(batch=batch, head_dim=D, num_heads=H, num_kv_heads=Hkv, kv_dtype=kvd,
+                                 max_ctx_len=max_ctx, block_size=16, max_blocks_per_seq=-(-max_ctx // 16),
+                                 **extra)
+                        p = sw.swattn_plan(d, n_q, window)
+                        table = 512 if p.variant == sw.SWATTN_VARIANT_MFMA else 256
+                        worst = _longest_split(p, n_q, H // Hkv, window, max_ctx)
+                        assert worst <= table, (D, H, Hkv, batch, max_ctx, n_q, window, p.as_dict(), worst)
+                        checked += 1
+    # the prefill entry point (n_q up to 512, 64-row chunks)
+    for max_ctx, window in ((4096, 188), (8192, 10 ** 6), (40000, 4096)):
+        d = desc(batch=1, kv_dtype=kvd, max_ctx_len=max_ctx, max_blocks_per_seq=-(-max_ctx // 16), **extra)
+        p = sw.swattn_prefill_plan(d, 512, window)
+        table = 512 if p.variant == sw.SWATTN_VARIANT_MFMA else 256
+        assert _longest_split(p, 512, 4, window, max_ctx) <= table, p.as_dict()
+        checked += 1
+    assert checked > 500

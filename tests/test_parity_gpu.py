@@ -114,6 +114,24 @@ def test_fused_merge_equals_merge_kernel(key, variant):
         assert int(ws[:sw.SWATTN_WORKSPACE_COUNTER_BYTES].count_nonzero()) == 0
 
 
+@pytest.mark.parametrize("D,n_q,window", [(64, 1, 10 ** 6), (256, 1, 10 ** 6), (256, 8, 10 ** 6), (128, 8, 5000),
+                                          (256, 8, 188)])
+def test_single_sequence_past_4096_keys(D, n_q, window):
+    # One sequence of 8192 positions.  Past 4096 keys a launch of a few units needs more
+    # than 8 splits to keep each split within its workgroup's 512-entry key table (full
+    # attention: 16 splits, merged by the last workgroup where the partials are small).
+    gu.log(f"[long context] D={D} n_q={n_q} window={window}")
+    w = synth.make_workload("long_ctx", B=1, H=8, Hkv=2, D=D, n_q=n_q, window=window, ctx=8192, bs=16, seed=12)
+    ref = gu.reference(w)
+    t = gu.upload(w)
+    got, plan = gu.run(w, t, out_f32=True)
+    keys = min(8192, window + n_q - 1)
+    assert plan.variant == sw.SWATTN_VARIANT_MFMA and plan.num_splits * 512 >= keys
+    gu.check(got, ref, w.kv_dtype, True, label=f"long D={D} n_q={n_q} W={window} plan {plan.as_dict()}")
+    got, _ = gu.run(w, t, out_f32=False)
+    gu.check(got, ref, w.kv_dtype, False, label=f"long D={D} n_q={n_q} W={window} bf16 out")
+
+
 @pytest.mark.parametrize("variant", [sw.SWATTN_VARIANT_MFMA, sw.SWATTN_VARIANT_VALU])
 def test_split_invariance_decode(variant):
     # plain decode (4 rows per KV head): a 16-row matrix-core tile with 12 padding rows,
