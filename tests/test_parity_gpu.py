@@ -203,6 +203,27 @@ def test_fuzz(case):
     gu.check(got, ref, w.kv_dtype, c["out_f32"] or c["qd"] == "f32", label=f"fz{c['idx']}")
 
 
+def fuzz_long_cases(n=10, seed=4321):
+    # contexts past 4096 positions: long windows need more than eight key splits
+    rng = np.random.default_rng(seed)
+    cases = []
+    for k in range(n):
+        n_q = int(rng.choice([1, 3, 8]))
+        qd, kd = DTYPES[k % len(DTYPES)]
+        B = int(rng.choice([1, 2]))
+        cases.append(dict(idx=k, n_q=n_q, window=int(rng.choice([188, 4500, 10 ** 6])),
+                          bs=int(rng.choice([16, 64, 300])), G=int(rng.choice([1, 4, 8])),
+                          Hkv=int(rng.choice([1, 2])), D=int(rng.choice([64, 128, 256])), qd=qd, kd=kd, B=B,
+                          ctx=[int(rng.integers(4097, 16001)) for _ in range(B)], out_f32=True,
+                          S=int(rng.choice([0, 0, 0, 40])), sentinels=False))
+    return cases
+
+
+@pytest.mark.parametrize("case", fuzz_long_cases(), ids=lambda c: f"fzl{c['idx']}")
+def test_fuzz_long_context(case):
+    test_fuzz(case)
+
+
 # ---------------------------------------------------------------------------
 # mask pattern: one-hot V rows turn the output into the softmax weights
 # ---------------------------------------------------------------------------
