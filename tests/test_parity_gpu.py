@@ -114,6 +114,48 @@ def test_fused_merge_equals_merge_kernel(key, variant):
         assert int(ws[:sw.SWATTN_WORKSPACE_COUNTER_BYTES].count_nonzero()) == 0
 
 
+@pytest.mark.parametrize("key,S_cycle", [("verify", (2, 4, 3, 8)), ("decode", (3, 8)), ("batched_fp8", (2,)),
+                                         ("batched_bf16", (3, 2))])
+def test_fused_merge_back_to_back_stress(key, S_cycle):
+    """64 fused-merge launches queued back to back on one stream, with no host
+    synchronisation between them, over eight query sets and a cycle of split counts on
+    one workspace: every output is bit-equal to the merge kernel's for its query set and
+    split count.  Hundreds of merge groups per launch, each combining partials written
+    by workgroups on other XCDs: a partial read before its writer's stores were visible,
+    or a counter the previous launch left non-zero, would show in some launch."""
+    w = synth.named_workload(key)
+    t = gu.upload(w)
+    mc = int(w.ctx_len.max())
+    q_sets = [(t["q"].float() * c).to(torch.bfloat16) for c in (1.0, -1.0, 0.5, -2.0, 0.25, 1.5, -0.75, 3.0)]
+
+    def call(q, S, merge, ws=None):
+        return sw.verify(q, t["k"], t["v"], t["bt"], t["ctx"], w.n_q, w.window, w.scale, mc,
+                         out_dtype=sw.SWATTN_F32, k_scale=t["ks"], v_scale=t["vs"], num_splits=S,
+                         merge=merge, workspace=ws)
+
+    expect = {}
+    ws_bytes = 0
+    for S in S_cycle:
+        for i, q in enumerate(q_sets):
+            out, plan = call(q, S, sw.SWATTN_MERGE_KERNEL)
+            assert plan.num_splits == S and plan.merge_grid > 0
+            expect[(i, S)] = out
+        ws_bytes = max(ws_bytes, plan.workspace_bytes)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=gu.DEV)
+    gu.log(f"[fused stress] {key} S cycle {S_cycle}, groups per launch "
+           f"{plan.grid // plan.num_splits}")
+    got = []
+    for n in range(64):
+        i, S = n % len(q_sets), S_cycle[(n // len(q_sets)) % len(S_cycle)]
+        out, plan = call(q_sets[i], S, sw.SWATTN_MERGE_FUSED, ws)
+        assert plan.fused_merge == 1 and plan.merge_grid == 0
+        got.append((i, S, out))
+    torch.cuda.synchronize()
+    bad = [(n, i, S) for n, (i, S, out) in enumerate(got) if not torch.equal(out, expect[(i, S)])]
+    assert not bad, f"{key}: fused != merge kernel in launches {bad[:8]}"
+    assert int(ws[:sw.SWATTN_WORKSPACE_COUNTER_BYTES].count_nonzero()) == 0
+
+
 @pytest.mark.parametrize("D,n_q,window", [(64, 1, 10 ** 6), (256, 1, 10 ** 6), (256, 8, 10 ** 6), (128, 8, 5000),
                                           (256, 8, 188)])
 def test_single_sequence_past_4096_keys(D, n_q, window):
