@@ -35,11 +35,13 @@ constexpr int kGatherMaxQRows = 512;         // Q rows of one workgroup
 
 #define LDS_ADDR(p) ((__attribute__((address_space(3))) void*)(p))
 
+// With the non-temporal cache policy, as the partition kernels' copies (64-row chunks
+// aside), which measured faster on every launch that reads each row once.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void gather16(const void* src, const void* lds_dst) {
     const uint32_t a = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)LDS_ADDR(lds_dst));
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(a), "v"(src) : "m0");
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt" ::"s"(a), "v"(src) : "m0");
 }
 #pragma clang diagnostic pop
 

@@ -129,6 +129,13 @@ struct Geo {
     // verify step's 147 KB per workgroup: 10.5 us with 4 waves, 8.2 us with 8; the
     // verify step itself: 9.7 -> 8.7 us warm, cold unchanged).
     static constexpr int kNL = RB == 1 ? kNWc : 0;
+    // Where two workgroups share a CU, their K/V and Q copies carry the non-temporal cache
+    // policy: batched bf16 27.5 -> 24.7 us, batched E4M3 20.0 -> 18.9 us, full context
+    // 4096 (32-key tiles) 48.2 -> 42.7 us.  Not in 64-row chunks, whose workgroups re-read
+    // a unit's window from L2 (prefill of 512 positions 67.8 -> 69.9 us with it), nor at
+    // one workgroup per CU, where it measured within +-1 us (verify, decode, full context
+    // 1024 and 2048).
+    static constexpr bool kStream = kBlocks == 2 && RB != 4;
     static constexpr int kNW = kNWc + kNL;
     static constexpr int kNT = kNW * 64;
     static constexpr int kShare = (kNiK + kNiV) / kNW;      // load instructions per wave per tile
@@ -225,12 +232,17 @@ __device__ __forceinline__ uint32_t lds_addr(const T* p) {
 // around it); it stays ordered with barriers and waits, which have side effects.
 // Every read of the destination is ordered by an explicit vmcnt wait in the
 // issuing wave and a barrier.  M0 holds the LDS base; nothing else in these
-// kernels uses M0.
+// kernels uses M0.  NT sets the non-temporal cache policy (a hint: the bytes read are
+// the same).
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
+template <bool NT>
 __device__ __forceinline__ void dma16(const void* src, uint32_t lds_dst) {
     const uint32_t a = __builtin_amdgcn_readfirstlane(lds_dst);
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(a), "v"(src) : "m0");
+    if constexpr (NT)
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt" ::"s"(a), "v"(src) : "m0");
+    else
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(a), "v"(src) : "m0");
 }
 #pragma clang diagnostic pop
 
@@ -300,9 +312,9 @@ __global__ __launch_bounds__((Geo<D, FP8, KT, RB, CS>::kNT), (Geo<D, FP8, KT, RB
             const unsigned char* src = reinterpret_cast<const unsigned char*>(p.q) +
                                        (((int64_t)b * p.n_q + i) * p.H + h) * G::kRowQ + ((pc ^ G::swz_q(row)) << 4);
             if constexpr (G::kQAlias)
-                dma16(src, lds_addr(&kst[NS - 1][j * 1024]));
+                dma16<G::kStream>(src, lds_addr(&kst[NS - 1][j * 1024]));
             else
-                dma16(src, lds_addr(&qst[j * 1024]));
+                dma16<G::kStream>(src, lds_addr(&qst[j * 1024]));
         }
     }
 
@@ -421,7 +433,7 @@ __global__ __launch_bounds__((Geo<D, FP8, KT, RB, CS>::kNT), (Geo<D, FP8, KT, RB
             if (j < j0 || j >= j1) continue;
             const int ins = wave * SH + j;       // compile-time j, wave-uniform ins
             const bool is_v = ins >= G::kNiK;
-            dma16(src[j], is_v ? lds_addr(&vst[t % NS][(ins - G::kNiK) * 1024]) : lds_addr(&kst[t % NS][ins * 1024]));
+            dma16<G::kStream>(src[j], is_v ? lds_addr(&vst[t % NS][(ins - G::kNiK) * 1024]) : lds_addr(&kst[t % NS][ins * 1024]));
         }
     };
 
@@ -484,7 +496,7 @@ __global__ __launch_bounds__((Geo<D, FP8, KT, RB, CS>::kNT), (Geo<D, FP8, KT, RB
         auto load_one = [=](int j, const unsigned char* from) __attribute__((always_inline)) {
             const int ins = wave * SH + j;       // compile-time j, wave-uniform ins
             const bool is_v = ins >= G::kNiK;
-            dma16(from, is_v ? lds_addr(&vst[tn % NS][(ins - G::kNiK) * 1024]) : lds_addr(&kst[tn % NS][ins * 1024]));
+            dma16<G::kStream>(from, is_v ? lds_addr(&vst[tn % NS][(ins - G::kNiK) * 1024]) : lds_addr(&kst[tn % NS][ins * 1024]));
         };
         if (loader) {
             if (prefetch) {
