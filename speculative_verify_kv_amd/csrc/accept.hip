@@ -32,6 +32,13 @@
 namespace swattn {
 namespace {
 
+// 16 logits' bytes with the non-temporal cache policy: every logit is read once (64
+// sequences x 8 positions x 262,144 bf16 logits: 52.2 -> 46.4 us; one sequence unchanged)
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream16(const void* p) {
+    return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p)));
+}
+
 __device__ __forceinline__ uint64_t argmax_key(float v, uint32_t index) {
     uint32_t u = __float_as_uint(v);
     if ((u & 0x7FFFFFFFu) == 0u) u = 0u;                          // -0 -> +0
@@ -94,7 +101,7 @@ __global__ __launch_bounds__(kBlockThreads) void argmax_chunks_kernel(AcceptPara
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     const int64_t vu = v + (int64_t)u * kBlockThreads * 8;
-                    w[u] = vu < v1 ? *reinterpret_cast<const uint4*>(L + vu) : make_uint4(0, 0, 0, 0);
+                    w[u] = vu < v1 ? load_stream16(L + vu) : make_uint4(0, 0, 0, 0);
                 }
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
@@ -140,7 +147,7 @@ __global__ __launch_bounds__(kBlockThreads) void argmax_chunks_kernel(AcceptPara
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     const int64_t vu = v + (int64_t)u * kBlockThreads * 4;
-                    f[u] = vu < v1 ? *reinterpret_cast<const float4*>(L + vu) : make_float4(0, 0, 0, 0);
+                    f[u] = vu < v1 ? __builtin_bit_cast(float4, load_stream16(L + vu)) : make_float4(0, 0, 0, 0);
                 }
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
