@@ -47,6 +47,9 @@ CASES = [
     dict(id="d128_g8", B=2, n_q=5, ctx=[2000, 190], D=128, H=16, Hkv=2),
     dict(id="bs1", B=2, n_q=8, ctx=[400, 9], bs=1, max_blocks=512),
     dict(id="bs300", B=2, n_q=8, ctx=[600, 301], bs=300, max_blocks=2, window=100),
+    # full attention past 4096 keys: more than eight splits per chunk
+    dict(id="long_full", B=1, n_q=8, ctx=[8192], window=10 ** 6, max_blocks=512),
+    dict(id="long_decode_d64", B=1, n_q=1, ctx=[9000], window=10 ** 6, max_blocks=563, D=64),
 ]
 
 
@@ -101,6 +104,8 @@ def test_append_verify_equals_append_then_verify(c):
     gu.log(f"  plan {plan.as_dict()}")
     if c["id"] in ("tall", "tall_many"):
         assert plan.rows_per_chunk == 64 and plan.tile_keys == (64 if c["id"] == "tall" else 32), plan.as_dict()
+    if c["id"].startswith("long"):
+        assert plan.num_splits > 8, plan.as_dict()
     stream = torch.cuda.current_stream().cuda_stream
     outs, caches = [], []
     for fused in (True, False):
