@@ -502,6 +502,9 @@ PREFILL_CASES = [
     dict(B=1, H=8, Hkv=2, D=256, n_q=512, window=4096, ctx=[512], bs=16, S=0, kv="bf16", f32=True),
     dict(B=2, H=8, Hkv=2, D=256, n_q=96, window=188, ctx=[1000, 300], bs=16, S=0, kv="e4m3", f32=False),
     dict(B=1, H=6, Hkv=2, D=64, n_q=65, window=17, ctx=[65], bs=1, S=0, kv="bf16", f32=True),
+    # past 4096 keys: 64-row chunks split more than eight ways, and an E4M3 cache
+    dict(B=1, H=8, Hkv=2, D=256, n_q=128, window=10 ** 6, ctx=[8192], bs=16, S=0, kv="bf16", f32=True),
+    dict(B=1, H=8, Hkv=2, D=256, n_q=100, window=6000, ctx=[7000], bs=16, S=0, kv="e4m3", f32=True),
 ]
 
 
