@@ -192,26 +192,39 @@ __global__ __launch_bounds__(kBlockThreads) void argmax_chunks_kernel(AcceptPara
     }
 }
 
-// One wave per sequence; lane i reduces position i's chunk keys.
+// One wave per sequence; lane i reduces position i's chunk keys.  Every lane fetches its
+// draft id up front, and the accepted count is the first lane whose draft differs from the
+// target's token (a wave ballot), so no load waits on a comparison: the scan of the drafts
+// one after another had made this kernel as long as the argmax pass (4.4 us).
+static_assert(kAcceptMaxNq <= 64, "one lane of a wave per position");
 __global__ __launch_bounds__(64) void accept_finalize_kernel(AcceptParams p) {
     const int b = blockIdx.x;
     const int lane = threadIdx.x;
-    __shared__ int tgt[kAcceptMaxNq];
+    const int n_drafts = p.n_q - 1;
+    const int draft = lane < n_drafts ? p.draft_ids[(int64_t)b * n_drafts + lane] : 0;
+    int id = 0;
     if (lane < p.n_q) {
         const uint64_t* part = p.partial + ((int64_t)b * p.n_q + lane) * p.nchunk;
         uint64_t k = 0;
-        for (int c = 0; c < p.nchunk; ++c) k = part[c] > k ? part[c] : k;
-        const int id = (int)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFu));
-        tgt[lane] = id;
+        int c = 0;
+        for (; c + 8 <= p.nchunk; c += 8) {                      // eight loads in flight
+            uint64_t v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = part[c + u];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) k = v[u] > k ? v[u] : k;
+        }
+        for (; c < p.nchunk; ++c) k = part[c] > k ? part[c] : k;
+        id = (int)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFu));
         p.target_ids[(int64_t)b * p.n_q + lane] = id;
     }
-    __syncthreads();
+    // draft j is accepted while it equals the target's token after input j
+    const uint64_t mismatch = __ballot(lane < n_drafts && draft != id);
+    const int a = mismatch != 0 ? __ffsll((unsigned long long)mismatch) - 1 : n_drafts;
+    const int next = __shfl(id, a, 64);
     if (lane == 0) {
-        const int32_t* d = p.draft_ids + (int64_t)b * (p.n_q - 1);
-        int a = 0;
-        while (a < p.n_q - 1 && d[a] == tgt[a]) ++a;
         p.accepted[b] = a;
-        p.next_token[b] = tgt[a];
+        p.next_token[b] = next;
     }
 }
 
