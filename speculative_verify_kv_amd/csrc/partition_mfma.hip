@@ -8,7 +8,7 @@
 // K row and compute the same scores; each loads its part of every V row); launches
 // with many rows per KV head take 64-row chunks, so that each K/V tile serves more
 // rows.  The split's keys are walked in tiles of 64 (or 32) through an LDS ring
-// filled by direct global-to-LDS loads.
+// filled by direct global-to-LDS loads (non-temporal where two workgroups share a CU).
 //
 // With 64-key tiles, compute wave w owns 16 query rows (a row block), one 32-key
 // half of every tile's keys, with an online softmax of its own, and a set of the
