@@ -452,6 +452,24 @@ def test_many_units_32_key_tiles(S):
     assert np.array_equal(first, again)
 
 
+@pytest.mark.parametrize("kv,B,n_q", [("bf16", 1024, 8), ("e4m3", 1024, 8), ("bf16", 256, 64)])
+def test_large_launch_sampled_sequences(kv, B, n_q):
+    # Launches several times larger than the CUs hold (2,048 workgroups: four rounds at
+    # two per CU), checked on a sample of sequences (first, last and spread), each
+    # against the oracle run on that sequence alone through the same caches.
+    gu.log(f"[large launch] {kv} B={B} n_q={n_q}")
+    w = synth.make_workload(f"large_{kv}_{B}", B=B, H=8, Hkv=2, D=256, n_q=n_q, window=188, ctx=None, bs=16,
+                            seed=31, kv_dtype=kv, recent=188 + n_q - 1, ctx_range=(n_q, 400), max_blocks=25)
+    got, plan = gu.run(w, out_f32=True)
+    gu.log(f"  plan {plan.as_dict()}")
+    assert plan.grid >= 2048, plan.as_dict()
+    for b in sorted({0, 1, B // 3, B // 2, 2 * B // 3, B - 2, B - 1}):
+        ref = oracle.attend(w.q[b:b + 1], w.k_cache, w.v_cache, w.block_table[b:b + 1], w.ctx_len[b:b + 1],
+                            w.n_q, w.window, w.scale, q_format=w.q_format, kv_format=w.kv_format,
+                            k_scale=w.k_scale, v_scale=w.v_scale)
+        gu.check(got[b:b + 1], ref, w.kv_dtype, True, label=f"large {kv} b={b}")
+
+
 # ---------------------------------------------------------------------------
 # 64-row chunks (bfloat16 caches, head_dim 256, Q^T loaded into registers; 64-key
 # tiles and eight waves while the grid fits the CUs, else 32-key tiles and four waves):
