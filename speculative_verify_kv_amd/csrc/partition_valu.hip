@@ -92,11 +92,45 @@ __device__ __forceinline__ int64_t valu_row_offset(const PartitionParams& p, int
     return (((int64_t)phys * p.Hkv + g) * p.bs + off) * (int64_t)p.D;
 }
 
+// Lane exchanges without the LDS crossbar (__shfl_xor goes through ds_bpermute, one
+// round trip through the LDS per step, which made the softmax of a handful of rows take
+// 1.3 us): DPP moves within each 16-lane row, then gfx950's lane-group swaps across rows.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+constexpr int kDppXor1 = 0xB1;    // quad_perm [1, 0, 3, 2]: lane l reads lane l ^ 1
+constexpr int kDppXor2 = 0x4E;    // quad_perm [2, 3, 0, 1]: lane l reads lane l ^ 2
+constexpr int kDppRor4 = 0x124;   // row_ror:4 within the 16-lane row
+constexpr int kDppRor8 = 0x128;   // row_ror:8
+
+// Sum over the 4 lanes of a quad (l & ~3 .. l | 3), every lane receiving it.
+__device__ __forceinline__ float quad_sum(float x) {
+    x += dpp_mov<kDppXor1>(x);
+    return x + dpp_mov<kDppXor2>(x);
+}
+
+// Max / sum over all 64 lanes of the wave, every lane receiving the result.
+template <bool MAX>
+__device__ __forceinline__ float wave_reduce(float x) {
+    const auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : a + b; };
+    x = op(x, dpp_mov<kDppXor1>(x));
+    x = op(x, dpp_mov<kDppXor2>(x));
+    x = op(x, dpp_mov<kDppRor4>(x));   // each lane: its quad and the next
+    x = op(x, dpp_mov<kDppRor8>(x));   // the whole 16-lane row
+    // rows l, l ^ 16, l ^ 32, l ^ 48: each swap returns the value and its partner's
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = op(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return op(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+
 template <int D, int KVT>
 __global__ __launch_bounds__(kBlockThreads) void partition_valu_kernel(PartitionParams p) {
     constexpr int RC = kValuRowsPerChunk;
     constexpr int KR = kValuKeyRound;
     constexpr int TPK = kBlockThreads / KR;   // 4 lanes per key in phase 1
+    static_assert(TPK == 4, "a key's lanes are one quad (quad_sum)");
     constexpr int DPT = D / TPK;              // dims per lane in phase 1
     constexpr int QPR = D / 4;                // phase-3 lanes per row
     constexpr int KGR = kBlockThreads / QPR;  // phase-3 key groups
@@ -214,9 +248,7 @@ __global__ __launch_bounds__(kBlockThreads) void partition_valu_kernel(Partition
                 float acc = 0.0f;
 #pragma unroll
                 for (int e = 0; e < DPT; ++e) acc = fmaf(qs[rr][part * DPT + e], kv[e], acc);
-                acc += __shfl_xor(acc, 1);
-                acc += __shfl_xor(acc, 2);
-                dots[rr] = acc;
+                dots[rr] = quad_sum(acc);
             }
             if (part == 0 && valid) {
 #pragma unroll
@@ -238,8 +270,7 @@ __global__ __launch_bounds__(kBlockThreads) void partition_valu_kernel(Partition
     for (int rr = wave; rr < RC; rr += kBlockThreads / kWaveSize) {
         float m = -INFINITY;
         for (int kk = lane; kk < nk; kk += kWaveSize) m = fmaxf(m, ps[rr][kk]);
-#pragma unroll
-        for (int sh = 1; sh < kWaveSize; sh <<= 1) m = fmaxf(m, __shfl_xor(m, sh));
+        m = wave_reduce<true>(m);
         const float mu = m == -INFINITY ? 0.0f : m;
         float sum = 0.0f;
         for (int kk = lane; kk < nk; kk += kWaveSize) {
@@ -247,8 +278,7 @@ __global__ __launch_bounds__(kBlockThreads) void partition_valu_kernel(Partition
             ps[rr][kk] = e;
             sum += e;
         }
-#pragma unroll
-        for (int sh = 1; sh < kWaveSize; sh <<= 1) sum += __shfl_xor(sum, sh);
+        sum = wave_reduce<false>(sum);
         if (lane == 0) {
             rstat[rr][0] = m;
             rstat[rr][1] = sum;
