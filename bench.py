@@ -26,7 +26,7 @@ kernel source, else null.  ``cpu_baseline``: the float64 oracle on this host.
 
 Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 20]
        [--workload verify|decode|batched_fp8|batched_bf16|wide_verify|fullctx_*|tiny_decode|prefill_512]
-       [--op attention|append_kv|accept|layer_graph]
+       [--op attention|append_kv|accept|layer_graph|gather_ceiling|read_ceiling]
 """
 import argparse
 import hashlib
@@ -378,15 +378,21 @@ def main():
     ap.add_argument("--no-extra", action="store_true",
                     help="default workload only: skip the batched-configuration measurements")
     ap.add_argument("--op", default="attention",
-                    choices=["attention", "append_kv", "accept", "layer_graph", "gather_ceiling"],
+                    choices=["attention", "append_kv", "accept", "layer_graph", "gather_ceiling", "read_ceiling"],
                     help="attention: swattn_verify / swattn_prefill (default); append_kv: swattn_append_kv "
                          "of the workload's new rows into its cache; accept: swattn_greedy_accept; "
                          "layer_graph: one decode step as a graph of per-layer calls; gather_ceiling: "
-                         "swattn_window_gather, the workload's data movement without arithmetic")
+                         "swattn_window_gather, the workload's data movement without arithmetic; "
+                         "read_ceiling: swattn_stream_read, a contiguous read of the workload's byte count")
     ap.add_argument("--vocab", type=int, default=262144, help="accept op: logits per position")
     ap.add_argument("--accept-batch", type=int, default=1, help="accept op: sequences per call")
     ap.add_argument("--gather-parts", type=int, default=1,
                     help="gather_ceiling op: workgroups per (problem, KV head), each a slice of its rows")
+    ap.add_argument("--unshuffled", action="store_true",
+                    help="attention and gather_ceiling ops: identity block tables (each sequence's blocks in "
+                         "order) instead of the workload's shuffled ones")
+    ap.add_argument("--read-grid", type=int, default=512,
+                    help="read_ceiling op: workgroups of the contiguous read (two per CU by default)")
     ap.add_argument("--calibrate-copy", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -439,6 +445,20 @@ def main():
                 "gather_parts": args.gather_parts}
         print(json.dumps(line), flush=True)
         return
+    if args.op == "read_ceiling":
+        r = measure_read(args.workload, args, torch, np, sw, synth, dev)
+        line = {"metric": "HBM read floor us/call (swattn_stream_read: a contiguous read of the verify call's "
+                          "algorithmic byte count)",
+                "value": r["value"], "unit": "us/call", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                "ms_per_step": round(r["value"] / 1e3, 6), "higher_is_better": False, "scaling": "weak",
+                "vs_baseline": None, "dtype": "u8", "data": "synthetic", "config": r["config"],
+                "roofline": r["roofline"], "timing": r["timing"], "xor_check": r["xor_check"],
+                "cpu_baseline": None, "read_grid": args.read_grid}
+        print(json.dumps(line), flush=True)
+        if not r["xor_check"]["ok"]:
+            print("bench.py: the contiguous read's xor check failed", file=sys.stderr)
+            sys.exit(1)
+        return
 
     res = measure_attention(args.workload, args, torch, np, sw, synth, dev)
     line = {
@@ -470,6 +490,9 @@ def main():
                                   "parts": 4,
                                   "what": "swattn_window_gather on the same inputs, four workgroups per "
                                           "(layer, KV head): the algorithmic bytes and paged loads, no arithmetic"}
+        c = measure_read(args.workload, args, torch, np, sw, synth, dev)
+        line["read_ceiling"] = _read_summary(c)
+        ok = ok and c["xor_check"]["ok"]
         # the batched configuration carries the bandwidth target: measured in the same run
         line["batched"] = {}
         for key in ("batched_fp8", "batched_bf16"):
@@ -484,11 +507,61 @@ def main():
                                                        "what": "swattn_window_gather on the same inputs: the same "
                                                                "bytes and paged loads, no arithmetic (one "
                                                                "workgroup per unit; more measured slower)"}}
-            ok = ok and r["parity_spot_check"]["ok"]
+            c = measure_read(key, args, torch, np, sw, synth, dev)
+            line["batched"][key]["read_ceiling"] = _read_summary(c)
+            ok = ok and r["parity_spot_check"]["ok"] and c["xor_check"]["ok"]
     print(json.dumps(line), flush=True)
     if not ok:
         print("bench.py: the spot check against the oracle failed", file=sys.stderr)
         sys.exit(1)
+
+
+def _read_summary(c):
+    return {"value": c["value"], "unit": "us/call", "frac": c["roofline"]["frac"], "grid": c["grid"],
+            "what": "swattn_stream_read: a contiguous read of the same algorithmic byte count by every CU "
+                    "(no block table, no per-unit workgroups): the time HBM alone sets"}
+
+
+def measure_read(key, args, torch, np, sw, synth, dev):
+    """Cold per-call time of swattn_stream_read over a contiguous device buffer of the
+    workload's algorithmic byte count (the floor HBM sets for that many bytes), timed
+    as the attention op in its read-only form; one call with the xor buffer is checked
+    against the host's xor first."""
+    w = synth.named_workload(key)
+    nbytes = algorithmic_bytes(w) // 16 * 16
+    grid = getattr(args, "read_grid", 512)
+    host = np.random.default_rng(11).integers(0, 1 << 32, size=nbytes // 4, dtype=np.uint32)
+    x = torch.from_numpy(host.view(np.int32)).to(dev)
+    xors = torch.zeros(grid * 4, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def launch(cs):
+        # timed without the xor buffer: the reads alone
+        sw.swattn_stream_read(x, nbytes, grid, None, cs)
+
+    # the same reads once with the workgroups' xors, checked against the host's
+    sw.swattn_stream_read(x, nbytes, grid, xors, stream.cuda_stream)
+    flush = ColdFlush(torch, dev)
+    for _ in range(args.warmup):
+        flush()
+        launch(stream.cuda_stream)
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(xors.cpu().numpy().view(np.uint32).reshape(grid, 4), axis=0)
+    want = np.bitwise_xor.reduce(host.reshape(-1, 4), axis=0) if nbytes else np.zeros(4, np.uint32)
+    t = time_calls(torch, dev, stream, launch, flush, args.steps, not args.no_graph)
+    cold_graph = t["cold_graph_us_per_call"]
+    achieved = nbytes / (cold_graph * 1e-6) / 1e9
+    res = {"value": round(cold_graph, 3), "grid": grid,
+           "config": {"workload": DESCRIPTIONS.get(key, w.name), "bytes": nbytes},
+           "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "algorithmic_bytes": nbytes,
+                        "kernel": "stream_read"},
+           "timing": t,
+           "xor_check": {"ok": bool(np.array_equal(got, want)),
+                         "what": "xor of every 16-byte chunk read, from the workgroups' results, against the host"}}
+    del x, xors, flush
+    torch.cuda.empty_cache()
+    return res
 
 
 def measure_attention(key, args, torch, np, sw, synth, dev, gather=False, gather_parts=None):
@@ -496,7 +569,9 @@ def measure_attention(key, args, torch, np, sw, synth, dev, gather=False, gather
     positions) on a named workload, its roofline fraction and an oracle spot check;
     with gather=True, of swattn_window_gather on the same inputs (no spot check)."""
     import oracle
-    w = synth.named_workload(key)
+    # tiny decode's single block is in order already
+    w = synth.named_workload(key, **({"shuffle": False} if getattr(args, "unshuffled", False) and
+                                     key != "tiny_decode" else {}))
 
     def to_dev(a, fmt):
         if fmt == "bf16":
@@ -548,11 +623,14 @@ def measure_attention(key, args, torch, np, sw, synth, dev, gather=False, gather
     cold_graph = t["cold_graph_us_per_call"]
     nbytes = algorithmic_bytes(w)
     achieved = nbytes / (cold_graph * 1e-6) / 1e9
+    config = {"workload": DESCRIPTIONS.get(key, w.name), "global_batch": w.B, "seq_len": int(max_ctx),
+              "parallelism": "none (1 GPU)"}
+    if not w.meta.get("shuffle", True) and key != "tiny_decode":
+        config["block_table"] = "identity (--unshuffled)"
     res = {
         "value": round(cold_graph, 3),
         "dtype": w.kv_dtype if w.kv_dtype != w.q_dtype else w.q_dtype,
-        "config": {"workload": DESCRIPTIONS.get(key, w.name), "global_batch": w.B, "seq_len": int(max_ctx),
-                   "parallelism": "none (1 GPU)"},
+        "config": config,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic(key),
                      "algorithmic_bytes": nbytes,

@@ -369,6 +369,23 @@ swattn_status_t swattn_window_gather(const swattn_desc_t* desc,
                                      const int32_t* block_table, const int32_t* ctx_len,
                                      int32_t n_q, int32_t window, int32_t parts, void* out, void* stream);
 
+/*
+ * swattn_stream_read — measurement aid: a plain contiguous read of `bytes` bytes at
+ * `src` (device memory, 16-byte aligned, `bytes` a non-negative multiple of 16), the
+ * time HBM alone sets for moving a call's byte count, to set beside
+ * swattn_window_gather's paged floor.  `grid` (1..65536) workgroups of 1024 threads
+ * stream it from the first cycle, thread t of the grid reading the 16-byte chunks
+ * t, t + 1024*grid, t + 2*1024*grid, ...; workgroup w writes xor_out[4w .. 4w+3] (device
+ * memory the caller owns, 4-byte aligned, 4*grid words): the xor, word by word, of the
+ * 16-byte chunks it read (zeros if none), so that a caller can check the read.  With
+ * xor_out NULL nothing is written (the form to time: reads only).  Returns
+ * SWATTN_ERR_NULL (src NULL), SWATTN_ERR_ALIGN or SWATTN_ERR_ARG before enqueuing
+ * anything when those conditions fail, SWATTN_ERR_HIP if the launch fails.  Context:
+ * "What each piece does, and why" in "The Fast Gemma Challenge: our verified-SOTA
+ * recipe, in full" (decode is bound by the KV cache's bandwidth).
+ */
+swattn_status_t swattn_stream_read(const void* src, int64_t bytes, int32_t grid, uint32_t* xor_out, void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* swattn_status_str(swattn_status_t status);
 

@@ -6,7 +6,8 @@ kernels of ``libswattn.so``.  The functions mirror the C ABI in
 ``swattn_workspace_init``, ``swattn_verify``, ``swattn_prefill_plan``, ``swattn_prefill``,
 ``swattn_append_kv``, ``swattn_append_verify``, ``swattn_greedy_accept_workspace``,
 ``swattn_greedy_accept``, ``swattn_check_inputs``, ``swattn_status_str``,
-``swattn_abi_version``, ``swattn_verify_noalloc``, ``swattn_window_gather``);
+``swattn_abi_version``, ``swattn_verify_noalloc``, ``swattn_window_gather``,
+``swattn_stream_read``);
 ``verify`` and ``prefill`` are conveniences that fill the descriptor from torch
 tensors and run on torch's current HIP stream.  There is no CPU
 fallback: if the library is missing, loading fails with an error.
@@ -36,7 +37,7 @@ SWATTN_STATIC_SCRATCH_BYTES = 16 << 20
 EXPORTED = ("swattn_plan", "swattn_workspace_bytes", "swattn_workspace_init", "swattn_verify", "swattn_prefill_plan",
             "swattn_prefill", "swattn_append_kv", "swattn_append_verify", "swattn_greedy_accept_workspace",
             "swattn_greedy_accept", "swattn_check_inputs", "swattn_status_str", "swattn_abi_version",
-            "swattn_verify_noalloc", "swattn_window_gather")
+            "swattn_verify_noalloc", "swattn_window_gather", "swattn_stream_read")
 
 
 class SwattnError(RuntimeError):
@@ -108,6 +109,9 @@ def lib():
                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
                                            ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
         L.swattn_window_gather.restype = ctypes.c_int
+        L.swattn_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                                         ctypes.c_void_p]
+        L.swattn_stream_read.restype = ctypes.c_int
         L.swattn_prefill_plan.argtypes = L.swattn_plan.argtypes
         L.swattn_prefill_plan.restype = ctypes.c_int
         L.swattn_prefill.argtypes = L.swattn_verify.argtypes
@@ -213,6 +217,13 @@ def swattn_window_gather(desc, q, k_cache, v_cache, block_table, ctx_len, n_q, w
                                     _ptr(ctx_len), int(n_q), int(window), int(parts), _ptr(out), _ptr(stream))
     if check and st != 0:
         raise SwattnError(st, "swattn_window_gather")
+    return st
+
+
+def swattn_stream_read(src, nbytes, grid, xor_out, stream=None, check=True):
+    st = lib().swattn_stream_read(_ptr(src), int(nbytes), int(grid), _ptr(xor_out), _ptr(stream))
+    if check and st != 0:
+        raise SwattnError(st, "swattn_stream_read")
     return st
 
 

@@ -1,5 +1,6 @@
 // swattn_window_gather: the data movement of a verify call without its arithmetic, as a
-// measurement of the floor that the paged layout and the launch shape set.
+// measurement of the floor that the paged layout and the launch shape set; and
+// swattn_stream_read: a contiguous read of a given size, the floor that HBM sets.
 //
 // `parts` workgroups per (problem b, KV head g) move exactly the bytes the verify
 // call's algorithmic count covers: the K and V rows of the union of its queries'
@@ -136,8 +137,77 @@ __global__ __launch_bounds__(kGatherThreads) void window_gather_kernel(GatherPar
     __syncthreads();
 }
 
+// A plain contiguous read, the other reference point: the same number of bytes as a
+// call moves, streamed by every CU from the first cycle (no table lookups before the
+// first request, no per-unit workgroups).  Thread t of the grid reads 16-byte chunks
+// t, t + T, t + 2T, ... (T threads in the grid), four in flight per round, with the
+// non-temporal cache policy; each workgroup writes the xor of the chunks it read, so
+// that a caller can check every byte was read, unless it is given no xor buffer (then
+// nothing is written: the final store's latency is no part of a read floor).
+constexpr int kReadThreads = 1024;
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// Xor over the wave's 64 lanes, wave-uniform: DPP moves within each 16-lane row (lane
+// l ^ 1, l ^ 2, then rotations by 4 and 8), then the four rows' first lanes.  A shuffle
+// per step would be an LDS round trip each (24 of them for four words), which at a few
+// chunks per thread is longer than the reads.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, CTRL, 0xF, 0xF, true);
+}
+__device__ __forceinline__ uint32_t wave_xor(uint32_t x) {
+    x ^= dpp_u32<0xB1>(x);    // quad_perm [1, 0, 3, 2]
+    x ^= dpp_u32<0x4E>(x);    // quad_perm [2, 3, 0, 1]
+    x ^= dpp_u32<0x124>(x);   // row_ror:4
+    x ^= dpp_u32<0x128>(x);   // row_ror:8
+    return __builtin_amdgcn_readlane(x, 0) ^ __builtin_amdgcn_readlane(x, 16) ^ __builtin_amdgcn_readlane(x, 32) ^
+           __builtin_amdgcn_readlane(x, 48);
+}
+
+__global__ __launch_bounds__(kReadThreads) void stream_read_kernel(const u32x4_t* __restrict__ src, int64_t n16,
+                                                                    uint32_t* __restrict__ xor_out) {
+    __shared__ u32x4_t part[kReadThreads / 64];
+    const int64_t stride = (int64_t)gridDim.x * kReadThreads;
+    u32x4_t acc = {0u, 0u, 0u, 0u};
+    int64_t i = (int64_t)blockIdx.x * kReadThreads + threadIdx.x;
+    for (; i + 3 * stride < n16; i += 4 * stride) {
+        const u32x4_t a = __builtin_nontemporal_load(src + i);
+        const u32x4_t b = __builtin_nontemporal_load(src + i + stride);
+        const u32x4_t c = __builtin_nontemporal_load(src + i + 2 * stride);
+        const u32x4_t d = __builtin_nontemporal_load(src + i + 3 * stride);
+        acc ^= (a ^ b) ^ (c ^ d);
+    }
+    for (; i < n16; i += stride) acc ^= __builtin_nontemporal_load(src + i);
+    if (xor_out == nullptr) return;   // the timing form: the reads alone (grid-uniform)
+    u32x4_t wx;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) wx[e] = wave_xor(acc[e]);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) part[wave] = wx;
+    __syncthreads();
+    if (threadIdx.x < 4) {
+        uint32_t r = 0;
+#pragma unroll
+        for (int w = 0; w < kReadThreads / 64; ++w) r ^= part[w][threadIdx.x];
+        xor_out[(int64_t)blockIdx.x * 4 + threadIdx.x] = r;
+    }
+}
+
 }  // namespace
 }  // namespace swattn
+
+extern "C" swattn_status_t swattn_stream_read(const void* src, int64_t bytes, int32_t grid, uint32_t* xor_out,
+                                              void* stream) {
+    using namespace swattn;
+    if (!src) return SWATTN_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(src) & 15) != 0 || (reinterpret_cast<uintptr_t>(xor_out) & 3) != 0)
+        return SWATTN_ERR_ALIGN;
+    if (bytes < 0 || bytes % 16 != 0 || grid < 1 || grid > 65536) return SWATTN_ERR_ARG;
+    hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)grid), dim3(kReadThreads), 0,
+                       reinterpret_cast<hipStream_t>(stream), reinterpret_cast<const u32x4_t*>(src), bytes / 16,
+                       xor_out);
+    return hipGetLastError() == hipSuccess ? SWATTN_OK : SWATTN_ERR_HIP;
+}
 
 extern "C" swattn_status_t swattn_window_gather(const swattn_desc_t* d, const void* q, const void* k_cache,
                                                 const void* v_cache, const int32_t* block_table,

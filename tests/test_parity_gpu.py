@@ -809,3 +809,53 @@ def test_window_gather_moves_the_data_and_writes_zeros(key, parts):
         st = sw.swattn_window_gather(desc, t["q"], t["k"], t["v"], t["bt"], t["ctx"], w.n_q, w.window, bad, out,
                                      stream, check=False)
         assert sw.STATUS[st] == "SWATTN_ERR_ARG"
+
+
+@pytest.mark.parametrize("n16,grid", [(0, 1), (1, 1), (1, 3), (1023, 1), (1025, 2), (3 * 1024 + 5, 1),
+                                      (4 * 2 * 1024 + 7, 2), (655_361, 512), (655_361, 37)])
+def test_stream_read_xor_per_workgroup(n16, grid):
+    # every 16-byte chunk i is read once, by workgroup (i mod 1024*grid) div 1024: each
+    # workgroup's xor matches the host's over exactly those chunks (zeros where none)
+    gu.log(f"[stream read] n16={n16} grid={grid}")
+    rng = np.random.default_rng(n16 * 7 + grid)
+    host = rng.integers(0, 1 << 32, size=(n16, 4), dtype=np.uint32)
+    x = torch.from_numpy(host.reshape(-1).view(np.int32)).to(gu.DEV) if n16 else torch.zeros(4, dtype=torch.int32,
+                                                                                              device=gu.DEV)
+    xors = torch.full((grid * 4,), -1, dtype=torch.int32, device=gu.DEV)
+    sw.swattn_stream_read(x, n16 * 16, grid, xors, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    got = xors.cpu().numpy().view(np.uint32).reshape(grid, 4)
+    want = np.zeros((grid, 4), dtype=np.uint32)
+    owner = (np.arange(n16) % (grid * 1024)) // 1024
+    for wg in np.unique(owner):
+        want[wg] = np.bitwise_xor.reduce(host[owner == wg], axis=0)
+    assert np.array_equal(got, want)
+
+
+def test_stream_read_rejects_bad_arguments():
+    x = torch.zeros(64, dtype=torch.int32, device=gu.DEV)
+    xors = torch.zeros(16, dtype=torch.int32, device=gu.DEV)
+    s = torch.cuda.current_stream().cuda_stream
+    for args, want in [((x, 24, 1, xors), "SWATTN_ERR_ARG"), ((x, -16, 1, xors), "SWATTN_ERR_ARG"),
+                       ((x, 64, 0, xors), "SWATTN_ERR_ARG"), ((x, 64, 65537, xors), "SWATTN_ERR_ARG"),
+                       ((x.data_ptr() + 4, 64, 1, xors), "SWATTN_ERR_ALIGN"),
+                       ((x, 64, 1, xors.data_ptr() + 2), "SWATTN_ERR_ALIGN"),
+                       ((None, 64, 1, xors), "SWATTN_ERR_NULL")]:
+        assert sw.STATUS[sw.swattn_stream_read(*args, s, check=False)] == want, args[1:3]
+    torch.cuda.synchronize()
+    assert int(xors.count_nonzero()) == 0
+
+
+def test_stream_read_without_xor_buffer():
+    # the timing form (no xor buffer) is accepted at any grid; the same call with the
+    # buffer still gives the host's xor afterwards
+    host = np.random.default_rng(5).integers(0, 1 << 32, size=(70_000, 4), dtype=np.uint32)
+    x = torch.from_numpy(host.reshape(-1).view(np.int32)).to(gu.DEV)
+    s = torch.cuda.current_stream().cuda_stream
+    for grid in (1, 5, 512):
+        assert sw.swattn_stream_read(x, host.size * 4, grid, None, s) == 0
+    xors = torch.zeros(8, dtype=torch.int32, device=gu.DEV)
+    sw.swattn_stream_read(x, host.size * 4, 2, xors, s)
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(xors.cpu().numpy().view(np.uint32).reshape(2, 4), axis=0)
+    assert np.array_equal(got, np.bitwise_xor.reduce(host, axis=0))
