@@ -391,6 +391,9 @@ def main():
     ap.add_argument("--unshuffled", action="store_true",
                     help="attention and gather_ceiling ops: identity block tables (each sequence's blocks in "
                          "order) instead of the workload's shuffled ones")
+    ap.add_argument("--window", type=int, default=0,
+                    help="attention and gather ops: another window for the window-188 workloads (their "
+                         "random recent rows follow it)")
     ap.add_argument("--read-grid", type=int, default=512,
                     help="read_ceiling op: workgroups of the contiguous read (two per CU by default)")
     ap.add_argument("--calibrate-copy", type=int, default=0,
@@ -516,6 +519,20 @@ def main():
         sys.exit(1)
 
 
+def workload_of(key, args, synth):
+    """The named workload, with the --unshuffled and --window overrides applied (tiny
+    decode's single block is in order already; full context and tiny decode keep their
+    windows)."""
+    kw = {}
+    if getattr(args, "unshuffled", False) and key != "tiny_decode":
+        kw["shuffle"] = False
+    if getattr(args, "window", 0):
+        if key == "tiny_decode" or key.startswith("fullctx"):
+            raise SystemExit(f"bench.py: --window does not apply to {key}")
+        kw["window"] = args.window
+    return synth.named_workload(key, **kw)
+
+
 def _read_summary(c):
     return {"value": c["value"], "unit": "us/call", "frac": c["roofline"]["frac"], "grid": c["grid"],
             "what": "swattn_stream_read: a contiguous read of the same algorithmic byte count by every CU "
@@ -527,7 +544,7 @@ def measure_read(key, args, torch, np, sw, synth, dev):
     workload's algorithmic byte count (the floor HBM sets for that many bytes), timed
     as the attention op in its read-only form; one call with the xor buffer is checked
     against the host's xor first."""
-    w = synth.named_workload(key)
+    w = workload_of(key, args, synth)
     nbytes = algorithmic_bytes(w) // 16 * 16
     grid = getattr(args, "read_grid", 512)
     host = np.random.default_rng(11).integers(0, 1 << 32, size=nbytes // 4, dtype=np.uint32)
@@ -569,9 +586,7 @@ def measure_attention(key, args, torch, np, sw, synth, dev, gather=False, gather
     positions) on a named workload, its roofline fraction and an oracle spot check;
     with gather=True, of swattn_window_gather on the same inputs (no spot check)."""
     import oracle
-    # tiny decode's single block is in order already
-    w = synth.named_workload(key, **({"shuffle": False} if getattr(args, "unshuffled", False) and
-                                     key != "tiny_decode" else {}))
+    w = workload_of(key, args, synth)
 
     def to_dev(a, fmt):
         if fmt == "bf16":
@@ -627,6 +642,8 @@ def measure_attention(key, args, torch, np, sw, synth, dev, gather=False, gather
               "parallelism": "none (1 GPU)"}
     if not w.meta.get("shuffle", True) and key != "tiny_decode":
         config["block_table"] = "identity (--unshuffled)"
+    if getattr(args, "window", 0):
+        config["window"] = f"{w.window} (--window)"
     res = {
         "value": round(cold_graph, 3),
         "dtype": w.kv_dtype if w.kv_dtype != w.q_dtype else w.q_dtype,

@@ -199,16 +199,16 @@ def _c0(**kw):
                          kv_dtype=F32, scale=1.0 / 8.0, recent=188, shuffle=False, **kw)
 
 
-def _c1(**kw):
-    return make_workload("verify_24layers_h8kv2_d256_bf16_ctx4096_w188_nq8", B=24, H=8,
-                         Hkv=2, D=256, n_q=8, window=188, ctx=4096, bs=16, seed=1,
-                         recent=188 + 8 - 1, **kw)
+def _c1(window=188, **kw):
+    return make_workload(f"verify_24layers_h8kv2_d256_bf16_ctx4096_w{window}_nq8", B=24, H=8,
+                         Hkv=2, D=256, n_q=8, window=window, ctx=4096, bs=16, seed=1,
+                         recent=window + 8 - 1, **kw)
 
 
-def _decode(**kw):
-    return make_workload("decode_24layers_h8kv2_d256_bf16_ctx4096_w188_nq1", B=24, H=8,
-                         Hkv=2, D=256, n_q=1, window=188, ctx=4096, bs=16, seed=6,
-                         recent=188, **kw)
+def _decode(window=188, **kw):
+    return make_workload(f"decode_24layers_h8kv2_d256_bf16_ctx4096_w{window}_nq1", B=24, H=8,
+                         Hkv=2, D=256, n_q=1, window=window, ctx=4096, bs=16, seed=6,
+                         recent=window, **kw)
 
 
 def _c2(ctx, **kw):
@@ -216,23 +216,23 @@ def _c2(ctx, **kw):
                          H=8, Hkv=2, D=256, n_q=8, window=4096, ctx=ctx, bs=16, seed=2, **kw)
 
 
-def _c3(**kw):
-    return make_workload("wideverify_24layers_h8kv2_d256_bf16_ctx4096_w188_nq64", B=24,
-                         H=8, Hkv=2, D=256, n_q=64, window=188, ctx=4096, bs=16, seed=3,
-                         recent=188 + 64 - 1, hot_frac=614 / 12288, **kw)
+def _c3(window=188, **kw):
+    return make_workload(f"wideverify_24layers_h8kv2_d256_bf16_ctx4096_w{window}_nq64", B=24,
+                         H=8, Hkv=2, D=256, n_q=64, window=window, ctx=4096, bs=16, seed=3,
+                         recent=window + 64 - 1, hot_frac=614 / 12288, **kw)
 
 
-def _c4(kv_dtype, **kw):
-    return make_workload(f"batched_256seq_h8kv2_d256_{kv_dtype}kv_ctxU188-4096_w188_nq8",
-                         B=256, H=8, Hkv=2, D=256, n_q=8, window=188, ctx=None, bs=16,
-                         seed=4, kv_dtype=kv_dtype, recent=188 + 8 - 1,
+def _c4(kv_dtype, window=188, **kw):
+    return make_workload(f"batched_256seq_h8kv2_d256_{kv_dtype}kv_ctxU188-4096_w{window}_nq8",
+                         B=256, H=8, Hkv=2, D=256, n_q=8, window=window, ctx=None, bs=16,
+                         seed=4, kv_dtype=kv_dtype, recent=window + 8 - 1,
                          ctx_range=(188, 4096), max_blocks=256, **kw)
 
 
-def _prefill(n_q, **kw):
-    return make_workload(f"prefill_24layers_h8kv2_d256_bf16_ctx4096_w188_nq{n_q}", B=24, H=8, Hkv=2,
-                         D=256, n_q=n_q, window=188, ctx=4096, bs=16, seed=5,
-                         recent=188 + n_q - 1, **kw)
+def _prefill(n_q, window=188, **kw):
+    return make_workload(f"prefill_24layers_h8kv2_d256_bf16_ctx4096_w{window}_nq{n_q}", B=24, H=8,
+                         Hkv=2, D=256, n_q=n_q, window=window, ctx=4096, bs=16, seed=5,
+                         recent=window + n_q - 1, **kw)
 
 
 # The five workloads of the build: tiny decode, single-stream verify, the
