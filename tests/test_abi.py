@@ -301,6 +301,35 @@ def test_verify_host_checks_return_before_launch():
     assert lib.swattn_check_inputs(ctypes.byref(d), None, 5 * A, 8, 188, None) == -1
 
 
+def test_measurement_aids_host_checks_return_before_launch():
+    # swattn_window_gather and swattn_stream_read refuse bad arguments on the host
+    lib = sw.lib()
+    d = desc()
+    A = 1 << 20   # fake, aligned, never dereferenced: every call below fails on the host
+
+    def gather(q=A, k=2 * A, v=3 * A, bt=4 * A, ctx=5 * A, n_q=8, window=188, parts=1, out=6 * A):
+        return sw.STATUS[lib.swattn_window_gather(ctypes.byref(d), q, k, v, bt, ctx, n_q, window, parts, out, None)]
+
+    assert gather(parts=0) == "SWATTN_ERR_ARG"
+    assert gather(parts=17) == "SWATTN_ERR_ARG"
+    assert gather(q=None) == "SWATTN_ERR_NULL"
+    assert gather(out=None) == "SWATTN_ERR_NULL"
+    assert gather(v=3 * A + 4) == "SWATTN_ERR_ALIGN"
+    assert gather(n_q=65) == "SWATTN_ERR_NQ"
+    assert gather(window=0) == "SWATTN_ERR_WINDOW"
+
+    def read(src=A, nbytes=1 << 16, grid=512, xor_out=2 * A):
+        return sw.STATUS[lib.swattn_stream_read(src, nbytes, grid, xor_out, None)]
+
+    assert read(src=None) == "SWATTN_ERR_NULL"
+    assert read(src=A + 8) == "SWATTN_ERR_ALIGN"
+    assert read(xor_out=2 * A + 2) == "SWATTN_ERR_ALIGN"
+    assert read(nbytes=24) == "SWATTN_ERR_ARG"
+    assert read(nbytes=-16) == "SWATTN_ERR_ARG"
+    assert read(grid=0) == "SWATTN_ERR_ARG"
+    assert read(grid=65537) == "SWATTN_ERR_ARG"
+
+
 def _longest_split(plan, n_q, G, window, ctx):
     """Most keys one workgroup scans under `plan` for a sequence of length ctx: the
     union of the windows of a row chunk's queries, in plan.num_splits near-equal parts
