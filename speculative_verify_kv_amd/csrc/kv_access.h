@@ -19,8 +19,12 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
     return (uint32_t)__builtin_bit_cast(uint16_t, h);
 }
 
+// Two floats -> packed bfloat16 bits (lo in bits 0-15), rounded as above: one two-source
+// conversion (two one-source conversions and their packing cost three more instructions).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
 // OCP E4M3 -> float, exactly, with gfx950's conversion instruction
@@ -37,7 +41,6 @@ __device__ __forceinline__ void e4m3x2_to_f32(uint32_t word, bool hi, float& a, 
 // gfx950's packed conversion with scale 1.0 (v_cvt_scalef32_pk_bf16_fp8) turns two
 // codes into two bfloat16s in one instruction; checked exhaustively against the
 // format definition for every code in every byte position.
-typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
 __device__ __forceinline__ uint4 e4m3x8_to_bf16x8(uint2 w) {
     const auto c = [](uint32_t word, bool hi) {
         return __builtin_bit_cast(uint32_t, hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, true)

@@ -609,13 +609,12 @@ __global__ __launch_bounds__((Geo<D, FP8, KT, RB, CS>::kNT), (Geo<D, FP8, KT, RB
             for (int e2 = 0; e2 < 2; ++e2) {
                 const float p0 = fast_exp2(sv[hh][2 * e2] - mu);
                 const float p1 = fast_exp2(sv[hh][2 * e2 + 1] - mu);
-                const uint32_t h0 = f32_to_bf16_bits(p0), h1 = f32_to_bf16_bits(p1);
+                const uint32_t hp = pack_bf16x2(p0, p1);
                 psum += p0 + p1;
-                wh[hh * 2 + e2] = h0 | (h1 << 16);
+                wh[hh * 2 + e2] = hp;
                 if constexpr (!kSingleP) {
-                    const uint32_t r0 = f32_to_bf16_bits(p0 - bf16_bits_to_f32(h0));
-                    const uint32_t r1 = f32_to_bf16_bits(p1 - bf16_bits_to_f32(h1));
-                    wl[hh * 2 + e2] = r0 | (r1 << 16);
+                    // the residuals against the rounded pair, unpacked in place
+                    wl[hh * 2 + e2] = pack_bf16x2(p0 - __uint_as_float(hp << 16), p1 - __uint_as_float(hp & 0xFFFF0000u));
                 } else {
                     wl[hh * 2 + e2] = 0u;
                 }
