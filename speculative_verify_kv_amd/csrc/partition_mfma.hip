@@ -439,6 +439,9 @@ __global__ __launch_bounds__((Geo<D, FP8, KT, RB, CS>::kNT), (Geo<D, FP8, KT, RB
 
     const int row_lo = qvalid ? max(0, pos0 + qi - p.window + 1) : 1;
     const int row_hi = qvalid ? pos0 + qi : 0;
+    // key t of the split (position k0 + t) counts for this row iff k0 + t - row_lo, as an
+    // unsigned number, is below row_cnt: the row's window cut at the split's last key
+    const int row_cnt = max(0, min(row_hi, k0 + nk - 1) - row_lo + 1);
 
     // The compiler cannot see the loads below, so a wait of its own for an earlier
     // load would count them as older: nothing it issued is left in flight from here.
@@ -567,11 +570,10 @@ __global__ __launch_bounds__((Geo<D, FP8, KT, RB, CS>::kNT), (Geo<D, FP8, KT, RB
 #pragma unroll
                 for (int e = 0; e < 4; ++e) sv[kb][e] = acc[e] * scale_log2;
             } else {
+                const int d0 = k0 + key_lo + kb * 16 + q4 * 4 - row_lo;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int tt = key_lo + kb * 16 + q4 * 4 + e;
-                    const int j = k0 + tt;
-                    const bool ok = tt < nk && j >= row_lo && j <= row_hi;
+                    const bool ok = (uint32_t)(d0 + e) < (uint32_t)row_cnt;
                     sv[kb][e] = ok ? acc[e] * scale_log2 : -INFINITY;
                 }
             }
