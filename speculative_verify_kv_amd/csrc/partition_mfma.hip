@@ -402,9 +402,20 @@ __global__ __launch_bounds__((Geo<D, FP8, KT, RB, CS>::kNT), (Geo<D, FP8, KT, RB
     }
     __syncthreads();   // source tables ready
 
-    // ---- this wave's loads: instructions wave*SH .. +SH-1 of a tile's 2*kNiK (K tile
-    //      first, then V tile); instruction i fills rows (i % kNiK)*kRpi .. +kRpi-1, and
-    //      lane l of it chunk l % kCpr of row (i % kNiK)*kRpi + l / kCpr
+    // ---- this wave's loads of a tile (kNiK K and kNiV V instructions; K instruction i
+    //      fills rows i*kRpi .. +kRpi-1, lane l of it chunk l % kCpr of row i*kRpi + l/kCpr,
+    //      V likewise).  Without loader waves every wave takes an equal share of each kind:
+    //      K instructions wave*SHK .. +SHK-1 as its loads 0 .. SHK-1, then V instructions
+    //      wave*SHV .. +SHV-1, so that whether a load is K or V is known at compile time and
+    //      its table entry is a fixed offset from one address per tile (prefill 64.8 ->
+    //      62.3 us).  With loader waves, instructions wave*SH .. +SH-1 of the K-then-V list:
+    //      the compute waves then issue K loads only (verify and decode measured slower
+    //      with the even split).
+    constexpr bool kEven = G::kNL == 0;
+    constexpr int SHK = kEven ? G::kNiK / G::kNW : 0;
+    constexpr int SHV = kEven ? G::kNiV / G::kNW : 0;
+    static_assert(!kEven || (SHK * G::kNW == G::kNiK && SHV * G::kNW == G::kNiV && SHK + SHV == SH),
+                  "every wave takes an equal share of the K and of the V instructions");
     const int rsub = lane / G::kCpr;
     const int pch = lane % G::kCpr;              // LDS chunk this lane fills (K)
     const int rsub_v = lane / G::kCprV;
@@ -413,16 +424,23 @@ __global__ __launch_bounds__((Geo<D, FP8, KT, RB, CS>::kNT), (Geo<D, FP8, KT, RB
     auto rows_of = [=](int t, const unsigned char** src) __attribute__((always_inline)) {   // this wave's SH source rows of tile t
 #pragma unroll
         for (int j = 0; j < SH; ++j) {
-            const int ins = wave * SH + j;
-            const bool is_v = ins >= G::kNiK;
-            if (is_v) {
-                const int row = (ins - G::kNiK) * G::kRpiV + rsub_v;
+            const int insk = kEven ? wave * SHK + j : wave * SH + j;                  // as K
+            const int insv = kEven ? wave * SHV + j - SHK : wave * SH + j - G::kNiK;  // as V
+            if (kEven ? j >= SHK : insk >= G::kNiK) {
+                const int row = insv * G::kRpiV + rsub_v;
                 src[j] = vptr[t * kT + row] + cs * G::kRowBV + ((pch_v ^ G::swz_v(row)) << 4);
             } else {
-                const int row = ins * G::kRpi + rsub;
+                const int row = insk * G::kRpi + rsub;
                 src[j] = kptr[t * kT + row] + ((pch ^ G::swz_k(row)) << 4);
             }
         }
+    };
+    // LDS slot of this wave's load j of a tile in stage st
+    auto slot_of = [=](int st, int j) __attribute__((always_inline)) {
+        if constexpr (kEven)
+            return j >= SHK ? lds_addr(&vst[st][(wave * SHV + j - SHK) * 1024]) : lds_addr(&kst[st][(wave * SHK + j) * 1024]);
+        const int ins = wave * SH + j;
+        return ins >= G::kNiK ? lds_addr(&vst[st][(ins - G::kNiK) * 1024]) : lds_addr(&kst[st][ins * 1024]);
     };
     // loads j0 .. j1-1 of this wave's share of tile t
     auto issue_range = [=](int t, int j0, int j1) __attribute__((always_inline)) {
@@ -431,9 +449,7 @@ __global__ __launch_bounds__((Geo<D, FP8, KT, RB, CS>::kNT), (Geo<D, FP8, KT, RB
 #pragma unroll
         for (int j = 0; j < SH; ++j) {
             if (j < j0 || j >= j1) continue;
-            const int ins = wave * SH + j;       // compile-time j, wave-uniform ins
-            const bool is_v = ins >= G::kNiK;
-            dma16<G::kStream>(src[j], is_v ? lds_addr(&vst[t % NS][(ins - G::kNiK) * 1024]) : lds_addr(&kst[t % NS][ins * 1024]));
+            dma16<G::kStream>(src[j], slot_of(t % NS, j));
         }
     };
 
@@ -497,9 +513,7 @@ __global__ __launch_bounds__((Geo<D, FP8, KT, RB, CS>::kNT), (Geo<D, FP8, KT, RB
         const unsigned char* src[SH];
         if (prefetch) rows_of(tn, src);
         auto load_one = [=](int j, const unsigned char* from) __attribute__((always_inline)) {
-            const int ins = wave * SH + j;       // compile-time j, wave-uniform ins
-            const bool is_v = ins >= G::kNiK;
-            dma16<G::kStream>(from, is_v ? lds_addr(&vst[tn % NS][(ins - G::kNiK) * 1024]) : lds_addr(&kst[tn % NS][ins * 1024]));
+            dma16<G::kStream>(from, slot_of(tn % NS, j));
         };
         if (loader) {
             if (prefetch) {
