@@ -178,20 +178,14 @@ __device__ __forceinline__ f32x4_t mfma_bf16(uint4 a, uint4 b, f32x4_t c) {
                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-// Max / sum over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four 16-lane groups holding
-// one score row), every lane receiving the result.  Each swap returns the value
-// and its partner's in some order; max and sum do not care which.
+// Max over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four 16-lane groups holding one score
+// row), every lane receiving the result.  Each swap returns the value and its partner's
+// in some order; the max does not care which.
 __device__ __forceinline__ float xgroup_max(float x) {
     const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
     const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
-}
-__device__ __forceinline__ float xgroup_sum(float x) {
-    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-    const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
 
 // 2^x by the hardware instruction alone.  Its arguments here are at most 8 (scores
@@ -488,6 +482,13 @@ __global__ __launch_bounds__((Geo<D, FP8, KT, RB, CS>::kNT), (Geo<D, FP8, KT, RB
         }
     }
     float m_run = -INFINITY, l_run = 0.0f;   // row l16 of block rb, keys of half kh
+    // The row sum of P accumulates on the matrix cores beside O^T: a matrix op with an
+    // all-ones A operand gives every lane its row's sum of the tile's (rounded) P terms, and
+    // the accumulator is rescaled with O^T.  That replaces eight adds and a cross-lane
+    // reduction per tile with one or two matrix ops, and the weights are normalised by the
+    // sum of exactly the terms that entered the PV product.
+    f32x4_t lacc = {0.0f, 0.0f, 0.0f, 0.0f};
+    const uint4 kOnes = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);   // bf16 1.0
     f32x4_t o[DB];                           // lane holds O^T[dcol0 + db*16 + 4*q4 + e][row l16]
     const int dcol0 = dh * DH;
 #pragma unroll
@@ -612,11 +613,10 @@ __global__ __launch_bounds__((Geo<D, FP8, KT, RB, CS>::kNT), (Geo<D, FP8, KT, RB
             const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.0f : m_new));
 #pragma unroll
             for (int db = 0; db < DB; ++db) o[db] = o[db] * alpha;
-            l_run *= alpha;
+            lacc = lacc * alpha;
             m_run = m_new;
         }
         const float mu = m_run == -INFINITY ? 0.0f : m_run;
-        float psum = 0.0f;
         // B operand of the PV step: k-slot hh*4 + e <-> key kbase_t + hh*16 + 4*q4 + e
         uint32_t wh[4], wl[4];
 #pragma unroll
@@ -626,7 +626,6 @@ __global__ __launch_bounds__((Geo<D, FP8, KT, RB, CS>::kNT), (Geo<D, FP8, KT, RB
                 const float p0 = fast_exp2(sv[hh][2 * e2] - mu);
                 const float p1 = fast_exp2(sv[hh][2 * e2 + 1] - mu);
                 const uint32_t hp = pack_bf16x2(p0, p1);
-                psum += p0 + p1;
                 wh[hh * 2 + e2] = hp;
                 if constexpr (!kSingleP) {
                     // the residuals against the rounded pair, unpacked in place
@@ -638,7 +637,6 @@ __global__ __launch_bounds__((Geo<D, FP8, KT, RB, CS>::kNT), (Geo<D, FP8, KT, RB
         }
         const uint4 ph = make_uint4(wh[0], wh[1], wh[2], wh[3]);
         const uint4 pl = make_uint4(wl[0], wl[1], wl[2], wl[3]);
-        l_run += xgroup_sum(psum);
 
         // ---- O^T = alpha O^T + V^T P^T ----------------------------------------------
         // Software-pipelined by hand: the V^T reads of step db+1 go out before the
@@ -686,7 +684,10 @@ __global__ __launch_bounds__((Geo<D, FP8, KT, RB, CS>::kNT), (Geo<D, FP8, KT, RB
 #pragma unroll
             for (int db = 0; db < DB; ++db) o[db] = mfma_bf16(va[db], pl, o[db]);
         }
+        lacc = mfma_bf16(kOnes, ph, lacc);
+        if constexpr (!kSingleP) lacc = mfma_bf16(kOnes, pl, lacc);
     }
+    l_run = lacc[0];                             // every element holds row l16's sum
 
     if constexpr (!G::kSplitKeys) {
         // ---- every wave holds all keys of its rows: normalise and write its columns
